@@ -1,0 +1,175 @@
+"""fp64 CPU oracle for the W4 (NVFP4) + dynamic LoRA linear -- TEST INFRASTRUCTURE ONLY.
+
+The arithmetic lives in ``oracle.cpp`` (plain C++, fp64, scalar loops); this module compiles it with
+g++ into ``liboracle.so`` and marshals numpy arrays through ctypes. It shares no code with the HIP
+library in ``bit_linear_dynamic_amd`` and never imports it. Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may use it.
+
+Method (FL2VA Turbo page, section "Implementation"):
+    y = NVFP4_base(x * pre_quant_scale) + strength * (alpha / rank) * B(A x)
+with the LoRA branch on the original bf16 activation. W4A4 variant: the base path's activation is
+itself quantized to NVFP4 per call (MiniMax-H3 Ultra Fast, "Kernel path"). Gate/up output feeds
+SiLU(gate) * up (same page, "Active optimization stack", MLP row).
+
+Every function here is pinned by tests/test_oracle_*.py against things other than itself: the
+format's published code tables and torch's float8 conversion, exact rational arithmetic on small
+shapes, numpy's fp64 matmul, rank-1 closed forms and identities. Nothing in the oracle is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "oracle.cpp")
+_LIB = os.path.join(_DIR, "liboracle.so")
+
+_CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c++17",
+           "-Wall", "-Wextra"]
+
+
+def build(out: str = _LIB, src: str = _SRC) -> str:
+    """Compile the oracle with g++ (never hipcc). ``src`` other than oracle.cpp is for the tests'
+    deliberately broken copies only."""
+    tmp = out + ".tmp"
+    cmd = ["g++", *_CFLAGS, src, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lib = None
+
+
+def _declare(lib):
+    i64, f64, f32, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_float, ctypes.c_int
+    vp = ctypes.c_void_p
+    lib.orc_e2m1_value.argtypes, lib.orc_e2m1_value.restype = [i32], f64
+    lib.orc_e4m3_value.argtypes, lib.orc_e4m3_value.restype = [i32], f64
+    lib.orc_e2m1_encode.argtypes, lib.orc_e2m1_encode.restype = [f64], i32
+    lib.orc_e4m3_encode_nonneg.argtypes, lib.orc_e4m3_encode_nonneg.restype = [f64], i32
+    lib.orc_quantize_nvfp4.argtypes = [vp, i64, i64, vp, vp, ctypes.POINTER(f32)]
+    lib.orc_quantize_nvfp4.restype = i32
+    lib.orc_prescale_f32.argtypes, lib.orc_prescale_f32.restype = [vp, vp, i64, i64, vp], None
+    lib.orc_dequant.argtypes, lib.orc_dequant.restype = [vp, vp, f64, i64, i64, vp], None
+    lib.orc_linear.argtypes = [vp, i64, i64, vp, vp, vp, f32, i64, vp, vp, i64, f64, f64, vp, vp, f32, vp]
+    lib.orc_linear.restype = i32
+    lib.orc_swiglu.argtypes, lib.orc_swiglu.restype = [vp, i64, i64, vp], None
+    lib.orc_num_threads.argtypes, lib.orc_num_threads.restype = [], i32
+    return lib
+
+
+def load(path: str | None = None):
+    """Load liboracle.so, building it first if it is missing or older than its source."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------------------------
+# numpy-facing wrappers (bf16 arrays are passed as their uint16 bit patterns)
+# --------------------------------------------------------------------------------------------
+
+def e2m1_value(code: int, lib=None) -> float:
+    return (lib or load()).orc_e2m1_value(int(code))
+
+
+def e4m3_value(code: int, lib=None) -> float:
+    return (lib or load()).orc_e4m3_value(int(code))
+
+
+def e2m1_encode(q: float, lib=None) -> int:
+    return (lib or load()).orc_e2m1_encode(float(q))
+
+
+def e4m3_encode(v: float, lib=None) -> int:
+    return (lib or load()).orc_e4m3_encode_nonneg(float(v))
+
+
+def quantize_nvfp4(v: np.ndarray, lib=None):
+    """fp32 [rows][K] -> (codes u8 [rows][K/2], scales u8 [rows][K/16], ts float)."""
+    v = _c(v, np.float32)
+    rows, K = v.shape
+    codes = np.zeros((rows, K // 2), np.uint8)
+    scales = np.zeros((rows, K // 16), np.uint8)
+    ts = ctypes.c_float(0.0)
+    rc = (lib or load()).orc_quantize_nvfp4(_ptr(v), rows, K, _ptr(codes), _ptr(scales), ctypes.byref(ts))
+    if rc != 0:
+        raise ValueError("orc_quantize_nvfp4: K must be a multiple of 16 and inputs finite")
+    return codes, scales, float(ts.value)
+
+
+def prescale_f32(x_bits: np.ndarray, pqs: np.ndarray | None, lib=None) -> np.ndarray:
+    """bf16 bits [rows][K], fp32 [K] -> fp32 [rows][K] = f32_rne(x * pqs)."""
+    x_bits = _c(x_bits, np.uint16)
+    rows, K = x_bits.shape
+    out = np.empty((rows, K), np.float32)
+    (lib or load()).orc_prescale_f32(_ptr(x_bits), _ptr(_c(pqs, np.float32)), rows, K, _ptr(out))
+    return out
+
+
+def dequant(codes: np.ndarray, scales: np.ndarray, ts: float = 1.0, lib=None) -> np.ndarray:
+    """(codes [rows][K/2], scales [rows][K/16]) -> fp64 [rows][K] = E2M1 * E4M3 * ts."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((rows, K), np.float64)
+    (lib or load()).orc_dequant(_ptr(codes), _ptr(scales), float(ts), rows, K, _ptr(out))
+    return out
+
+
+def linear(x_bits, pqs, codes, scales, ts, A_bits=None, B_bits=None, rank=0, alpha=0.0, strength=0.0,
+           act_codes=None, act_scales=None, ts_a=1.0, lib=None) -> np.ndarray:
+    """fp64 y [M][N] = base + strength*alpha/rank * B(A x)  (see oracle.cpp, orc_linear)."""
+    x_bits = _c(x_bits, np.uint16)
+    M, K = x_bits.shape
+    codes = _c(codes, np.uint8)
+    N = codes.shape[0]
+    y = np.empty((M, N), np.float64)
+    rc = (lib or load()).orc_linear(
+        _ptr(x_bits), M, K, _ptr(_c(pqs, np.float32)), _ptr(codes), _ptr(_c(scales, np.uint8)), float(ts), N,
+        _ptr(_c(A_bits, np.uint16)), _ptr(_c(B_bits, np.uint16)), int(rank), float(alpha), float(strength),
+        _ptr(_c(act_codes, np.uint8)), _ptr(_c(act_scales, np.uint8)), float(ts_a), _ptr(y))
+    if rc != 0:
+        raise ValueError("orc_linear: bad shape")
+    return y
+
+
+def swiglu(y: np.ndarray, lib=None) -> np.ndarray:
+    """fp64 [M][2F] -> fp64 [M][F] = SiLU(gate) * up, gate = y[:, :F], up = y[:, F:]."""
+    y = _c(y, np.float64)
+    M, N2 = y.shape
+    h = np.empty((M, N2 // 2), np.float64)
+    (lib or load()).orc_swiglu(_ptr(y), M, N2 // 2, _ptr(h))
+    return h
+
+
+def num_threads(lib=None) -> int:
+    return (lib or load()).orc_num_threads()
+
+
+def nvfp4_weight_fixture(w: np.ndarray, lib=None):
+    """Synthetic NVFP4 weight from an fp32 [N][K] array: the same quantizer with pqs = 1."""
+    return quantize_nvfp4(np.asarray(w, np.float32), lib=lib)
+
+
+def w4a4_activation(x_bits, pqs, lib=None):
+    """The W4A4 base path's activation: NVFP4 of f32_rne(x * pqs) with a per-call global scale."""
+    return quantize_nvfp4(prescale_f32(x_bits, pqs, lib=lib), lib=lib)

@@ -1,0 +1,246 @@
+// oracle.cpp -- plain, slow fp64 CPU reference for the W4 (NVFP4) + dynamic LoRA linear.
+//
+// TEST INFRASTRUCTURE ONLY. This file is the yardstick the HIP path is measured against. Only the
+// test suite, the smoke check and the benchmark's CPU-baseline leg may load it; the library under
+// bit_linear_dynamic_amd/ never includes, links or calls it, and it shares no code with it.
+//
+// What it computes (FL2VA Turbo page, section "Implementation"):
+//     output = NVFP4_base(x) + strength * (alpha / rank) * B(A(x))
+// where the base path sees the activation multiplied by the checkpoint's per-input-channel
+// pre_quant_scale and the bf16 LoRA branch sees the ORIGINAL activation (same section), and the
+// LoRA delta is never folded into the 4-bit weights.
+//
+// The pages name the weight format only as "NVFP4" (FL2VA Turbo, first paragraph; MiniMax-H3
+// Ultra Fast, "Active optimization stack" table). The element and scale encodings used here are the
+// public definitions of that format: E2M1 elements (bias 1, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6),
+// one E4M3 "FN" scale per 16 consecutive K-elements (bias 7, no infinities, NaN = S.1111.111,
+// largest finite 448), and one fp32 per-tensor scale applied by multiplication on decode.
+//
+// Everything below is written for obviousness, not speed: scalar loops, fp64 accumulation in
+// ascending k, nearest-value searches over the whole code table. OpenMP only splits independent
+// output rows across threads; it does not change any output's arithmetic.
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+// bf16 bit pattern -> exact double (bf16 is the top half of an IEEE binary32).
+double bf16_to_double(uint16_t h) {
+  uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return static_cast<double>(f);
+}
+
+}  // namespace
+
+extern "C" {
+
+// ------------------------------------------------------------------------------------------------
+// Element and scale decoders (closed forms of the two 8-bit-or-less minifloats).
+// ------------------------------------------------------------------------------------------------
+
+// E2M1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit. Exponent 0 is subnormal (0 or 0.5).
+double orc_e2m1_value(int code) {
+  const int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  const double mag = (e == 0) ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -mag : mag;
+}
+
+// E4M3 "FN": sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal
+// (m/8 * 2^-6); all-ones exponent with all-ones mantissa is NaN; there are no infinities.
+double orc_e4m3_value(int code) {
+  const int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return std::nan("");
+  const double mag = (e == 0) ? std::ldexp(m / 8.0, -6) : std::ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Encoders: round-to-nearest, ties to the code with an even (zero) mantissa LSB, saturating.
+// The argument is the real number to encode; callers pass exact values or fp64 quotients that are
+// provably on the same side of every rounding midpoint as the exact quotient.
+// ------------------------------------------------------------------------------------------------
+
+// Magnitude code 0..7 of the E2M1 value nearest |q|; |q| >= 6 saturates to 6 (code 7).
+static int e2m1_nearest_magnitude(double a) {
+  if (a >= 6.0) return 7;
+  int lo = 0;
+  for (int c = 0; c < 8; ++c)
+    if (orc_e2m1_value(c) <= a) lo = c;
+  if (lo == 7) return 7;
+  const int hi = lo + 1;
+  const double mid = 0.5 * (orc_e2m1_value(lo) + orc_e2m1_value(hi));  // exact: short dyadics
+  if (a < mid) return lo;
+  if (a > mid) return hi;
+  return (lo & 1) ? hi : lo;  // tie: the code whose mantissa bit is 0
+}
+
+// E2M1 code of q. A result of magnitude zero is encoded as +0 (code 0) whatever the sign of q.
+int orc_e2m1_encode(double q) {
+  const int mag = e2m1_nearest_magnitude(std::fabs(q));
+  if (mag == 0) return 0;
+  return (q < 0.0) ? (0x8 | mag) : mag;
+}
+
+// E4M3 code of a non-negative v; v >= 448 saturates to 448 (code 0x7E), never to NaN.
+int orc_e4m3_encode_nonneg(double v) {
+  if (!(v > 0.0)) return 0;
+  if (v >= 448.0) return 0x7E;
+  int lo = 0;
+  for (int c = 0; c <= 0x7E; ++c)
+    if (orc_e4m3_value(c) <= v) lo = c;
+  const int hi = lo + 1;  // lo < 0x7E because v < 448
+  const double mid = 0.5 * (orc_e4m3_value(lo) + orc_e4m3_value(hi));
+  if (v < mid) return lo;
+  if (v > mid) return hi;
+  return (lo & 1) ? hi : lo;
+}
+
+// ------------------------------------------------------------------------------------------------
+// NVFP4 quantizer (dynamic activation quantization of the W4A4 variant, and the synthetic-weight
+// fixture). MiniMax-H3 Ultra Fast, "Kernel path": activations are quantized to NVFP4 on every call.
+// Reading of the format's scale rules (plain reading, stated here because the pages give none):
+//   ts     = f32_rne(amax(|v|) / (6 * 448))       (1 if the tensor is all zero)
+//   s_b    = E4M3_rne_satfinite(amax_b / (6 * ts))  per block of 16 along K
+//   code   = E2M1_rne_sat(v / (E4M3(s_b) * ts))     (all codes 0 when s_b decodes to 0)
+// Each quotient is the exact real quotient rounded once. fp64 realizes that: the numerators have
+// at most 24 significant bits and the divisors at most 28, so a quotient that is not exactly a
+// rounding midpoint lies much farther from one than fp64's division error, and one that is exactly
+// a midpoint is computed exactly. For the fp32 tensor scale, rounding the correctly rounded fp64
+// quotient to fp32 is itself a correct rounding (53 >= 2*24 + 2).
+// Layout: codes [rows][K/2] with the even k in the low nibble; scales [rows][K/16].
+// Returns 0, or -1 if K is not a multiple of 16 or an input is not finite.
+// ------------------------------------------------------------------------------------------------
+int orc_quantize_nvfp4(const float* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                       float* ts_out) {
+  if (K % 16 != 0 || rows < 0) return -1;
+  double amax = 0.0;
+  for (int64_t i = 0; i < rows * K; ++i) {
+    if (!std::isfinite(v[i])) return -1;
+    amax = std::fmax(amax, std::fabs(static_cast<double>(v[i])));
+  }
+  const float ts = (amax == 0.0) ? 1.0f : static_cast<float>(amax / 2688.0);
+  *ts_out = ts;
+  const double six_ts = 6.0 * static_cast<double>(ts);  // exact
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < K / 16; ++b) {
+      const float* blk = v + r * K + b * 16;
+      double amax_b = 0.0;
+      for (int i = 0; i < 16; ++i) amax_b = std::fmax(amax_b, std::fabs(static_cast<double>(blk[i])));
+      const int sc = orc_e4m3_encode_nonneg(amax_b / six_ts);
+      scales[r * (K / 16) + b] = static_cast<uint8_t>(sc);
+      const double d = orc_e4m3_value(sc) * static_cast<double>(ts);  // exact (4 x 24 bits)
+      for (int i = 0; i < 16; i += 2) {
+        const int c0 = (d == 0.0) ? 0 : orc_e2m1_encode(static_cast<double>(blk[i]) / d);
+        const int c1 = (d == 0.0) ? 0 : orc_e2m1_encode(static_cast<double>(blk[i + 1]) / d);
+        codes[r * (K / 2) + b * 8 + i / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
+      }
+    }
+  }
+  return 0;
+}
+
+// Activation value the W4A4 quantizer sees: v = f32_rne(f32(x) * pqs[k]) (pqs NULL means 1).
+// The product of a bf16 and an fp32 is exact in fp64, so one cast gives the single rounding.
+void orc_prescale_f32(const uint16_t* x, const float* pqs, int64_t rows, int64_t K, float* v) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k) {
+      const double p = pqs ? static_cast<double>(pqs[k]) : 1.0;
+      v[r * K + k] = static_cast<float>(bf16_to_double(x[r * K + k]) * p);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Dequantization: out[r][k] = E2M1(code[r][k]) * E4M3(scale[r][k/16]) * ts, in fp64 (exact: at most
+// 2 + 4 + 24 significant bits). ts = 1 gives the bare E2M1 x E4M3 product.
+// ------------------------------------------------------------------------------------------------
+void orc_dequant(const uint8_t* codes, const uint8_t* scales, double ts, int64_t rows, int64_t K,
+                 double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k) {
+      const uint8_t byte = codes[r * (K / 2) + k / 2];
+      const int c = (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+      out[r * K + k] = orc_e2m1_value(c) * orc_e4m3_value(scales[r * (K / 16) + k / 16]) * ts;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// The linear itself, one output element at a time, fp64, ascending k.
+//   base[m][n]  = sum_k act[m][k] * Wd[n][k]
+//   where act = x (*) pqs                                (W4A16: FL2VA Turbo, "Implementation")
+//      or act = E2M1(acode) * E4M3(ascale) * ts_a        (W4A4: dynamically quantized activation)
+//   t[m][j]     = sum_k x[m][k] * A[j][k]                 (original, unscaled x)
+//   delta[m][n] = sum_j t[m][j] * B[n][j]
+//   y           = base + (strength * alpha / rank) * delta
+// x: bf16 [M][K]; pqs: fp32 [K] or NULL; codes/scales: weight [N][K/2] / [N][K/16]; ts: fp32;
+// A: bf16 [rank][K]; B: bf16 [N][rank]; y: fp64 [M][N]. rank == 0 or A == NULL means no adapter.
+// act_codes/act_scales (may be NULL): the W4A4 activation [M][K/2] / [M][K/16] with scale ts_a.
+// ------------------------------------------------------------------------------------------------
+int orc_linear(const uint16_t* x, int64_t M, int64_t K, const float* pqs, const uint8_t* codes,
+               const uint8_t* scales, float ts, int64_t N, const uint16_t* A, const uint16_t* B,
+               int64_t rank, double alpha, double strength, const uint8_t* act_codes,
+               const uint8_t* act_scales, float ts_a, double* y) {
+  if (K % 16 != 0 || M < 0 || N < 0 || rank < 0) return -1;
+  std::vector<double> Wd(static_cast<size_t>(N * K));
+  orc_dequant(codes, scales, static_cast<double>(ts), N, K, Wd.data());
+  std::vector<double> act(static_cast<size_t>(M * K));
+  if (act_codes) {
+    orc_dequant(act_codes, act_scales, static_cast<double>(ts_a), M, K, act.data());
+  } else {
+    for (int64_t m = 0; m < M; ++m)
+      for (int64_t k = 0; k < K; ++k)
+        act[m * K + k] = bf16_to_double(x[m * K + k]) * (pqs ? static_cast<double>(pqs[k]) : 1.0);
+  }
+  const bool lora = (A != nullptr && B != nullptr && rank > 0);
+  const double c = lora ? strength * alpha / static_cast<double>(rank) : 0.0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m) {
+    std::vector<double> t(static_cast<size_t>(lora ? rank : 0));
+    for (int64_t j = 0; lora && j < rank; ++j) {
+      double s = 0.0;
+      for (int64_t k = 0; k < K; ++k) s += bf16_to_double(x[m * K + k]) * bf16_to_double(A[j * K + k]);
+      t[j] = s;
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      double base = 0.0;
+      for (int64_t k = 0; k < K; ++k) base += act[m * K + k] * Wd[n * K + k];
+      double delta = 0.0;
+      for (int64_t j = 0; lora && j < rank; ++j) delta += t[j] * bf16_to_double(B[n * rank + j]);
+      y[m * N + n] = base + c * delta;
+    }
+  }
+  return 0;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Fused gate/up epilogue (MiniMax-H3 Ultra Fast, "Kernel path" and the MLP row of "Active
+// optimization stack"): the fused [gate; up] projection output y [M][2F] becomes
+//   h[m][j] = SiLU(y[m][j]) * y[m][F + j],   SiLU(z) = z / (1 + exp(-z)),   in fp64.
+// ------------------------------------------------------------------------------------------------
+void orc_swiglu(const double* y, int64_t M, int64_t F, double* h) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t j = 0; j < F; ++j) {
+      const double g = y[m * 2 * F + j], u = y[m * 2 * F + F + j];
+      h[m * F + j] = g / (1.0 + std::exp(-g)) * u;
+    }
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+}  // extern "C"

@@ -1,0 +1,409 @@
+"""Pins of the fp64 oracle: each check sets the oracle against something that is not the oracle.
+
+Independent sources used here:
+  * the published code tables of the format (tests/golden/nvfp4_format.txt) and torch's own
+    float8_e4m3fn conversion (a library routine) for decoding and for RNE encoding of E4M3;
+  * exact rational arithmetic (fractions.Fraction) with brute-force nearest-value search over the
+    whole code table, for the encoders and the quantizer (the oracle instead brackets the value
+    and compares with the midpoint in fp64);
+  * numpy's fp64 matmul on an independently decoded weight, for the contraction;
+  * closed forms: identity activations, one-hot activations against rank-1 adapters, zero weights;
+  * torch's SiLU in fp64 and the identity SiLU(z) - SiLU(-z) = z.
+
+Every pin is a function of the loaded oracle library (``lib``) so that tests/test_oracle_mutants.py
+can re-run all of them against deliberately broken builds of the oracle and show each break is
+caught. A pin raises AssertionError when the oracle disagrees.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------------------------------------
+# independent references
+# ------------------------------------------------------------------------------------------------
+
+def read_format_tables():
+    tables, cur = {}, None
+    with open(os.path.join(GOLDEN, "nvfp4_format.txt")) as f:
+        for raw in f:
+            line = raw.split("#")[0].strip()
+            if not line:
+                continue
+            if line.startswith("["):
+                cur = line.strip("[]")
+                tables[cur] = {}
+                continue
+            code, val = line.split()
+            tables[cur][int(code, 0)] = float(val)
+    return tables["e2m1"], tables["e4m3"]
+
+
+E2M1_GOLDEN, E4M3_LANDMARKS = read_format_tables()
+E2M1_ARRAY = np.array([E2M1_GOLDEN[c] for c in range(16)], np.float64)
+
+
+def e4m3_torch(codes) -> np.ndarray:
+    """Decode E4M3FN codes with torch's float8_e4m3fn dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def e4m3_encode_torch(values) -> np.ndarray:
+    """RNE-encode non-negative values <= 464 with torch's float8_e4m3fn cast."""
+    t = torch.tensor(np.asarray(values, np.float64), dtype=torch.float64).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def decode_independent(codes: np.ndarray, scales: np.ndarray, ts: float) -> np.ndarray:
+    """NVFP4 -> fp64 with the golden E2M1 table and torch's E4M3 (low nibble = even k)."""
+    rows = codes.shape[0]
+    nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(rows, -1)
+    sc = np.repeat(e4m3_torch(scales), 16, axis=1)
+    return E2M1_ARRAY[nib] * sc * float(ts)
+
+
+E2M1_FRAC = {c: Fraction(E2M1_GOLDEN[c]) for c in range(8)}
+E4M3_FRAC = {c: Fraction(float(v)) for c, v in enumerate(e4m3_torch(np.arange(0x7F, dtype=np.uint8)))}
+
+
+def nearest_code(value: Fraction, table: dict) -> int:
+    """Brute force: the code whose value is nearest; on a tie the code with even LSB (mantissa)."""
+    best = None
+    for c, v in table.items():
+        d = abs(value - v)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def round_to_f32(fr: Fraction) -> float:
+    """Correctly rounded (ties to even) binary32 of a non-negative rational, normal or subnormal."""
+    if fr == 0:
+        return 0.0
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    while Fraction(2) ** e > fr:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= fr:
+        e += 1
+    e = max(e, -126)
+    q = fr / Fraction(2) ** (e - 23)
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return float(Fraction(n) * Fraction(2) ** (e - 23))
+
+
+def quantize_exact(v: np.ndarray):
+    """NVFP4 quantization of an fp32 [rows][K] array in exact rationals (reading of the scale rules:
+    tensor scale = amax/(6*448) rounded to fp32; block scale = E4M3 nearest to amax_b/(6*ts);
+    element = E2M1 nearest to v/(scale*ts), saturating; zero block scale -> zero codes)."""
+    rows, K = v.shape
+    fr = [[Fraction(float(a)) for a in row] for row in v]
+    amax = max((abs(a) for row in fr for a in row), default=Fraction(0))
+    ts = Fraction(1) if amax == 0 else Fraction(round_to_f32(amax / 2688))
+    codes = np.zeros((rows, K // 2), np.uint8)
+    scales = np.zeros((rows, K // 16), np.uint8)
+    for r in range(rows):
+        for b in range(K // 16):
+            blk = fr[r][16 * b:16 * b + 16]
+            s = nearest_code(max(abs(a) for a in blk) / (6 * ts), E4M3_FRAC)
+            scales[r, b] = s
+            d = E4M3_FRAC[s] * ts
+            for i, a in enumerate(blk):
+                if d == 0:
+                    c = 0
+                else:
+                    mag = nearest_code(abs(a) / d, E2M1_FRAC)
+                    c = 0 if mag == 0 else (mag | (8 if a < 0 else 0))
+                codes[r, 8 * b + i // 2] |= c << (4 * (i % 2))
+    return codes, scales, float(ts)
+
+
+def bits_of(values) -> np.ndarray:
+    """fp64 values exactly representable in bf16 -> bf16 bit patterns (asserts exactness)."""
+    t = torch.tensor(np.asarray(values, np.float64))
+    b = t.to(torch.bfloat16)
+    assert torch.equal(b.to(torch.float64), t), "value not exact in bf16"
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def random_bf16(shape, std, rng) -> np.ndarray:
+    return bits_of(torch.tensor(rng.standard_normal(shape) * std).to(torch.bfloat16).to(torch.float64).numpy())
+
+
+def random_nvfp4(N, K, rng, std=0.02, lib=None):
+    w = (rng.standard_normal((N, K)) * std).astype(np.float32)
+    return oracle.quantize_nvfp4(w, lib=lib)
+
+
+# ------------------------------------------------------------------------------------------------
+# pins: codec
+# ------------------------------------------------------------------------------------------------
+
+def pin_e2m1_table(lib):
+    for c in range(16):
+        got, want = oracle.e2m1_value(c, lib), E2M1_GOLDEN[c]
+        assert got == want and np.signbit(got) == np.signbit(want), (c, got, want)
+
+
+def pin_e4m3_vs_torch(lib):
+    want = e4m3_torch(np.arange(256, dtype=np.uint8))
+    got = np.array([oracle.e4m3_value(c, lib) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def pin_e4m3_landmarks(lib):
+    for c, v in E4M3_LANDMARKS.items():
+        got = oracle.e4m3_value(c, lib)
+        if np.isnan(v):
+            assert np.isnan(got), hex(c)
+        else:
+            assert got == v and np.signbit(got) == np.signbit(v), (hex(c), got, v)
+
+
+def pin_e4m3_encode_vs_torch(lib):
+    rng = np.random.default_rng(11)
+    finite = e4m3_torch(np.arange(0x7F, dtype=np.uint8))
+    mids = (finite[:-1] + finite[1:]) / 2
+    vals = np.concatenate([finite, mids, rng.uniform(0, 464, 2000), np.exp(rng.uniform(-12, 6, 2000)),
+                           [448.0, 455.0, 464.0]])
+    want = e4m3_encode_torch(vals)
+    got = np.array([oracle.e4m3_encode(v, lib) for v in vals], np.uint8)
+    assert np.array_equal(got, want), vals[got != want][:8]
+    for v in (465.0, 1e6, 1e30):  # saturating, where torch would give NaN
+        assert oracle.e4m3_encode(v, lib) == 0x7E
+
+
+def pin_e2m1_encode_hand_vectors(lib):
+    # midpoints of the E2M1 grid round to the neighbour with mantissa bit 0
+    cases = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6,
+             0.2499: 0, 0.2501: 1, 0.7499: 1, 0.7501: 2, 1.2501: 3, 1.7499: 3, 2.5001: 5, 3.4999: 5,
+             4.9999: 6, 5.0001: 7, 6.0: 7, 7.0: 7, 1e9: 7, 0.0: 0, 0.1: 0}
+    for q, c in cases.items():
+        assert oracle.e2m1_encode(q, lib) == c, (q, c)
+        want_neg = 0 if c == 0 else (c | 8)
+        assert oracle.e2m1_encode(-q, lib) == want_neg, (-q, want_neg)
+
+
+def pin_e2m1_encode_bruteforce(lib):
+    rng = np.random.default_rng(12)
+    vals = np.concatenate([rng.uniform(-7, 7, 3000), np.arange(-28, 29) / 4.0])
+    for v in vals:
+        mag = nearest_code(abs(Fraction(float(v))), E2M1_FRAC)
+        want = 0 if mag == 0 else (mag | (8 if v < 0 else 0))
+        assert oracle.e2m1_encode(v, lib) == want, v
+
+
+# ------------------------------------------------------------------------------------------------
+# pins: quantizer
+# ------------------------------------------------------------------------------------------------
+
+def pin_quantizer_exact_random(lib):
+    rng = np.random.default_rng(13)
+    arrays = [
+        rng.standard_normal((3, 64)).astype(np.float32),
+        (rng.standard_normal((2, 48)) * np.exp(rng.uniform(-20, 5, (2, 48)))).astype(np.float32),
+        np.zeros((1, 32), np.float32),
+        np.concatenate([np.zeros(16), rng.standard_normal(16) * 1e-8]).reshape(1, 32).astype(np.float32),
+    ]
+    for v in arrays:
+        got = oracle.quantize_nvfp4(v, lib=lib)
+        want = quantize_exact(v)
+        assert np.array_equal(got[0], want[0]), "codes"
+        assert np.array_equal(got[1], want[1]), "scales"
+        assert got[2] == want[2], "tensor scale"
+
+
+def pin_quantizer_hand_block(lib):
+    # amax = 2688 = 6 * 448 makes the tensor scale exactly 1 and block 0's scale 448 (code 0x7E);
+    # every other element then sits on a known point of the E2M1 grid times 448.
+    q = [2688 / 448, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, -6.0]
+    # block 1: amax 6.375 = 6 * 1.0625, an E4M3 midpoint (1.0 | 1.125) -> scale 1.0 (code 0x38)
+    blk1 = [6.375, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, -6.0, 0.0, -0.0, 0.24, 5.5, 0.75, -0.25, 2.9, 6.2]
+    v = np.array([[x * 448 for x in q] + blk1], np.float32)
+    codes, scales, ts = oracle.quantize_nvfp4(v, lib=lib)
+    assert ts == 1.0
+    assert list(scales[0]) == [0x7E, 0x38]
+    want0 = [7, 0, 2, 2, 4, 4, 6, 6, 0, 10, 10, 12, 12, 14, 14, 15]
+    want1 = [7, 1, 2, 3, 4, 5, 6, 15, 0, 0, 0, 7, 2, 0, 5, 7]
+    nib = np.stack([codes[0] & 0xF, codes[0] >> 4], axis=-1).reshape(-1)
+    assert list(nib[:16]) == want0, list(nib[:16])
+    assert list(nib[16:]) == want1, list(nib[16:])
+
+
+def pin_quantizer_bounds(lib):
+    rng = np.random.default_rng(14)
+    v = (rng.standard_normal((8, 256)) * 3).astype(np.float32)
+    codes, scales, ts = oracle.quantize_nvfp4(v, lib=lib)
+    assert ts == np.float32(np.float64(np.abs(v).max()) / 2688)
+    deq = decode_independent(codes, scales, ts)
+    d = np.repeat(e4m3_torch(scales), 16, axis=1) * ts
+    # every element is within half a grid step (at most 1 * d, between 4 and 6) of its value
+    assert np.all(np.abs(deq - v) <= 1.0 * d + 1e-30)
+    # the block maximum does not saturate beyond the grid: |v| <= 6 d (1 + 2^-4) per element
+    assert np.all(np.abs(v) <= 6 * d * (1 + 2 ** -4))
+
+
+# ------------------------------------------------------------------------------------------------
+# pins: dequantization layout and the linear
+# ------------------------------------------------------------------------------------------------
+
+def pin_dequant_vs_independent(lib):
+    rng = np.random.default_rng(15)
+    codes = rng.integers(0, 256, (5, 24), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (5, 3), dtype=np.uint8)
+    got = oracle.dequant(codes, scales, 0.375, lib=lib)
+    want = decode_independent(codes, scales, 0.375)
+    assert np.array_equal(got, want) and np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def _lora_case(rng, M, K, N, r, lib):
+    x = random_bf16((M, K), 1.0, rng)
+    pqs = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    codes, scales, ts = random_nvfp4(N, K, rng, lib=lib)
+    A = random_bf16((r, K), 0.01 * 8, rng)
+    B = random_bf16((N, r), 0.01 * 8, rng)
+    return x, pqs, codes, scales, ts, A, B
+
+
+def pin_linear_vs_numpy(lib):
+    rng = np.random.default_rng(16)
+    for (M, K, N, r, alpha, strength) in [(5, 48, 7, 3, 1.5, 0.7), (9, 64, 33, 16, 16.0, 1.0), (4, 32, 6, 2, 8.0, -0.5)]:
+        x, pqs, codes, scales, ts, A, B = _lora_case(rng, M, K, N, r, lib)
+        got = oracle.linear(x, pqs, codes, scales, ts, A, B, r, alpha, strength, lib=lib)
+        xv, Av, Bv = bf16_values(x), bf16_values(A), bf16_values(B)
+        Wd = decode_independent(codes, scales, ts)
+        want = (xv * pqs.astype(np.float64)) @ Wd.T + strength * alpha / r * ((xv @ Av.T) @ Bv.T)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+        # adapter absent: base only
+        got0 = oracle.linear(x, pqs, codes, scales, ts, lib=lib)
+        np.testing.assert_allclose(got0, (xv * pqs.astype(np.float64)) @ Wd.T, rtol=1e-12, atol=1e-14)
+
+
+def pin_linear_exact_fractions(lib):
+    # tiny shapes with few-bit dyadic inputs: every fp64 operation is exact, so the oracle must
+    # equal the rational result bit for bit
+    rng = np.random.default_rng(17)
+    M, K, N, r = 3, 32, 4, 2
+    x = bits_of(rng.integers(-8, 9, (M, K)) / 4.0)
+    pqs = (2.0 ** rng.integers(-1, 2, K)).astype(np.float32)
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.choice(np.array([0x30, 0x38, 0x3C, 0x40, 0x44], np.uint8), (N, K // 16))
+    ts = 0.25
+    A = bits_of(rng.integers(-4, 5, (r, K)) / 8.0)
+    B = bits_of(rng.integers(-4, 5, (N, r)) / 8.0)
+    alpha, strength = 3.0, 0.5
+    got = oracle.linear(x, pqs, codes, scales, ts, A, B, r, alpha, strength, lib=lib)
+    xv, Av, Bv = bf16_values(x), bf16_values(A), bf16_values(B)
+    Wd = decode_independent(codes, scales, ts)
+    c = Fraction(strength) * Fraction(alpha) / r
+    for m in range(M):
+        t = [sum(Fraction(xv[m, k]) * Fraction(Av[j, k]) for k in range(K)) for j in range(r)]
+        for n in range(N):
+            base = sum(Fraction(xv[m, k]) * Fraction(float(pqs[k])) * Fraction(Wd[n, k]) for k in range(K))
+            delta = sum(t[j] * Fraction(Bv[n, j]) for j in range(r))
+            assert Fraction(got[m, n]) == base + c * delta, (m, n)
+
+
+def pin_identity_activation(lib):
+    # x = I (S = K), pqs = 1, no adapter: y[m][n] = ts * Wq[n][m], one product per output
+    rng = np.random.default_rng(18)
+    K, N = 32, 5
+    x = bits_of(np.eye(K))
+    codes, scales, ts = random_nvfp4(N, K, rng, lib=lib)
+    got = oracle.linear(x, None, codes, scales, ts, lib=lib)
+    assert np.array_equal(got, decode_independent(codes, scales, ts).T)
+
+
+def pin_rank1_closed_form(lib):
+    rng = np.random.default_rng(19)
+    K, N = 48, 6
+    codes, scales, ts = random_nvfp4(N, K, rng, lib=lib)
+    Wd = decode_independent(codes, scales, ts)
+    pqs = (2.0 ** rng.integers(-1, 2, K)).astype(np.float32)
+    k = 37
+    x = bits_of(np.eye(K)[k:k + 1])
+    a = rng.integers(-4, 5, K) / 8.0
+    b = rng.integers(-4, 5, N) / 8.0
+    # rank 1, alpha 2, strength 0.5: y[n] = Wd[n,k] pqs[k] + 0.5 * 2 * a_k b_n
+    got = oracle.linear(x, pqs, codes, scales, ts, bits_of(a[None, :]), bits_of(b[:, None]), 1, 2.0, 0.5, lib=lib)
+    assert np.array_equal(got[0], Wd[:, k] * float(pqs[k]) + 1.0 * a[k] * b)
+    # rank 4, alpha 1: the factor alpha / rank = 1/4 must be applied
+    A4 = rng.integers(-4, 5, (4, K)) / 8.0
+    B4 = rng.integers(-4, 5, (N, 4)) / 8.0
+    got4 = oracle.linear(x, pqs, codes, scales, ts, bits_of(A4), bits_of(B4), 4, 1.0, 1.0, lib=lib)
+    assert np.array_equal(got4[0], Wd[:, k] * float(pqs[k]) + 0.25 * (B4 @ A4[:, k]))
+
+
+def pin_prescale_base_only(lib):
+    # zero weights: the output is the pure LoRA term and does not depend on pqs (original x);
+    # no adapter: the output does not depend on A or B
+    rng = np.random.default_rng(20)
+    M, K, N, r = 4, 32, 5, 3
+    x, pqs, codes, scales, ts, A, B = _lora_case(rng, M, K, N, r, lib)
+    zc = np.zeros_like(codes)
+    y1 = oracle.linear(x, pqs, zc, scales, ts, A, B, r, 2.0, 1.0, lib=lib)
+    y2 = oracle.linear(x, pqs * 2, zc, scales, ts, A, B, r, 2.0, 1.0, lib=lib)
+    assert np.array_equal(y1, y2)
+    xv, Av, Bv = bf16_values(x), bf16_values(A), bf16_values(B)
+    np.testing.assert_allclose(y1, 2.0 / r * (xv @ Av.T) @ Bv.T, rtol=1e-12, atol=1e-15)
+    assert np.any(y1 != 0)
+
+
+def pin_strength_linearity(lib):
+    rng = np.random.default_rng(21)
+    x, pqs, codes, scales, ts, A, B = _lora_case(rng, 6, 64, 9, 4, lib)
+    y = {s: oracle.linear(x, pqs, codes, scales, ts, A, B, 4, 4.0, s, lib=lib) for s in (0.0, 0.5, 1.0)}
+    np.testing.assert_allclose(y[1.0] - y[0.0], 2 * (y[0.5] - y[0.0]), rtol=1e-9, atol=1e-14)
+    assert np.array_equal(y[0.0], oracle.linear(x, pqs, codes, scales, ts, lib=lib))
+
+
+def pin_w4a4_base(lib):
+    rng = np.random.default_rng(22)
+    M, K, N, r = 5, 64, 7, 4
+    x, pqs, codes, scales, ts, A, B = _lora_case(rng, M, K, N, r, lib)
+    ac, asc, ts_a = oracle.w4a4_activation(x, pqs, lib=lib)
+    # the activation the quantizer sees is f32_rne(x * pqs), compared with torch's fp32 product
+    v = oracle.prescale_f32(x, pqs, lib=lib)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
+    assert np.array_equal(v, (xt * torch.from_numpy(pqs)).numpy())
+    want_c, want_s, want_ts = quantize_exact(v)
+    assert np.array_equal(ac, want_c) and np.array_equal(asc, want_s) and ts_a == want_ts
+    got = oracle.linear(x, pqs, codes, scales, ts, A, B, r, 4.0, 1.0, act_codes=ac, act_scales=asc, ts_a=ts_a, lib=lib)
+    Xd = decode_independent(ac, asc, ts_a)
+    Wd = decode_independent(codes, scales, ts)
+    xv, Av, Bv = bf16_values(x), bf16_values(A), bf16_values(B)
+    np.testing.assert_allclose(got, Xd @ Wd.T + (xv @ Av.T) @ Bv.T, rtol=1e-12, atol=1e-14)
+
+
+def pin_swiglu(lib):
+    rng = np.random.default_rng(23)
+    y = rng.standard_normal((3, 10)) * 4
+    got = oracle.swiglu(y, lib=lib)
+    g, u = torch.from_numpy(y[:, :5]), torch.from_numpy(y[:, 5:])
+    np.testing.assert_allclose(got, (torch.nn.functional.silu(g) * u).numpy(), rtol=1e-14, atol=1e-300)
+    z = rng.standard_normal(8) * 5
+    ones = np.ones(8)
+    sp = oracle.swiglu(np.concatenate([z, ones])[None, :], lib=lib)[0]
+    sn = oracle.swiglu(np.concatenate([-z, ones])[None, :], lib=lib)[0]
+    np.testing.assert_allclose(sp - sn, z, rtol=1e-14, atol=1e-14)
+    assert oracle.swiglu(np.array([[0.0, 3.0]]), lib=lib)[0, 0] == 0.0
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,204 @@
+"""Throughput of the W4 (NVFP4) + dynamic LoRA linear on one MI355X.
+
+One step = the four projections of one synthetic MiniMax-H3 DiT block at the packed sequence length
+S = 37726 (fused QKV 18432x6144 r=384, attention-out 6144x6144 r=128, fused gate/up 32768x6144 r=128,
+down 6144x16384 r=128; rank = alpha; strength 1; adapter active), each through h3q_linear: LoRA-down
+(+ x * pqs) and the W4 GEMM with the folded LoRA-up and the epilogue. Inputs are synthetic (seeded),
+resident in HBM before timing starts.
+
+  metric  effective TFLOP/s = sum over projections of 2 S N K + 2 S r (K + N), per second of wall time
+  roofline  the main GEMM kernel (MFMA-bound): 2 S N (K + r) FLOP per launch over its HIP-event time
+  cpu_baseline  the fp64 oracle on a bounded row sample of the same workload, on the host cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--S 37726] [--cpu-rows R | --no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU (published 2.5 PF)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--S", type=int, default=37726)
+    ap.add_argument("--cpu-rows", type=int, default=24, help="rows per projection in the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    return ap.parse_args()
+
+
+def build_block(S, device):
+    """Pack the four projections (weights quantized on the device by h3q_quantize_nvfp4 from
+    N(0, 0.02) draws) and register one adapter each; returns per-projection state."""
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+    from bit_linear_dynamic_amd import synth
+    from bit_linear_dynamic_amd import workloads as wl
+
+    projs = []
+    xs = {}
+    for i, p in enumerate(wl.BLOCK):
+        w = synth.weight_fp32(p.N, p.K, synth.seed_of(3, i, synth.W), device).to(torch.bfloat16)
+        codes, scales, ts = h3q.h3q_quantize_nvfp4(w)
+        torch.cuda.synchronize()
+        del w
+        handle = h3q.h3q_pack_weight(codes.cpu(), scales.cpu(), ts.item(), p.N, p.K,
+                                     h3q.H3Q_PACK_GATE_UP if p.gate_up else 0)
+        host = (codes.cpu(), scales.cpu(), ts.item())
+        del codes, scales
+        A, B = synth.lora_factors(p.N, p.K, p.rank, synth.seed_of(3, i, synth.A1), synth.seed_of(3, i, synth.B1), device)
+        h3q.h3q_register_adapter(handle, 1, A.cpu(), B.cpu(), p.rank, p.alpha)
+        if p.K not in xs:
+            xs[p.K] = (synth.activation(S, p.K, synth.seed_of(3, i, synth.X), device),
+                       synth.pre_quant_scale(p.K, synth.seed_of(3, i, synth.PQS), device))
+        x, pqs = xs[p.K]
+        y = torch.empty((S, p.N), dtype=torch.bfloat16, device=device)
+        projs.append(dict(p=p, handle=handle, x=x, pqs=pqs, y=y, host=host, A=A, B=B))
+    torch.cuda.synchronize()
+    return projs
+
+
+def step(projs, stream):
+    import bit_linear_dynamic_amd as h3q
+    for d in projs:
+        h3q.h3q_linear(d["x"], d["pqs"], d["handle"], 1, 1.0, y=d["y"], stream=stream)
+
+
+def cpu_baseline(projs, S, rows_per_proj):
+    """The oracle as it stands, on rows_per_proj evenly spaced rows of each projection (incl. the
+    first and the last row), timed with a wall clock around the oracle calls only."""
+    import numpy as np
+
+    import oracle
+    from bit_linear_dynamic_amd import synth
+    from bit_linear_dynamic_amd import workloads as wl
+
+    rows = np.unique(np.linspace(0, S - 1, rows_per_proj).astype(np.int64))
+    lib = oracle.load()
+    inputs = []
+    for d in projs:
+        p = d["p"]
+        idx = __import__("torch").from_numpy(rows).to(d["x"].device)
+        xb = synth.bf16_bits(d["x"].index_select(0, idx))
+        codes, scales, ts = d["host"]
+        inputs.append((xb, d["pqs"].cpu().numpy(), codes.numpy(), scales.numpy(), ts,
+                       synth.bf16_bits(d["A"]), synth.bf16_bits(d["B"]), p))
+    t0 = time.perf_counter()
+    for xb, pqs, codes, scales, ts, A, B, p in inputs:
+        oracle.linear(xb, pqs, codes, scales, ts, A, B, p.rank, p.alpha, 1.0, lib=lib)
+    dt = time.perf_counter() - t0
+    flops = sum(wl.effective_flops(len(rows), p) for *_, p in inputs)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"{len(rows)} evenly spaced rows (first and last included) of each of the 4 projections "
+                      f"at S={S}, adapter active; {dt:.1f} s wall for {flops / 1e9:.1f} GFLOP effective "
+                      f"(whole-weight fp64 decode per projection included)",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
+              "(the projection shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+    from bit_linear_dynamic_amd import workloads as wl
+
+    device = "cuda"
+    S = args.S
+    print(f"bench: building the four projections at S={S}", file=sys.stderr, flush=True)
+    projs = build_block(S, device)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        step(projs, stream)
+    torch.cuda.synchronize()
+    print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    h3q.h3q_timing_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(projs, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    gemm_ms, gemm_n = h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM)
+    down_ms, down_n = h3q.h3q_timing_get(h3q.H3Q_KERNEL_LORA_DOWN)
+    h3q.h3q_timing_enable(False)
+
+    ms_per_step = total_ms / args.steps
+    flops_step = sum(wl.effective_flops(S, d["p"]) for d in projs)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    gemm_flops_launch = sum(2 * S * d["p"].N * (d["p"].K + d["p"].rank) for d in projs) / len(projs)
+    gemm_avg_ms = gemm_ms / max(gemm_n, 1)
+    achieved = gemm_flops_launch / (gemm_avg_ms * 1e-3) / 1e12
+
+    # per-projection breakdown (separate, untimed-above pass with timing on)
+    per_proj = {}
+    for d in projs:
+        h3q.h3q_timing_enable(True)
+        for _ in range(3):
+            h3q.h3q_linear(d["x"], d["pqs"], d["handle"], 1, 1.0, y=d["y"])
+        torch.cuda.synchronize()
+        g, gn = h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM)
+        l, ln = h3q.h3q_timing_get(h3q.H3Q_KERNEL_LORA_DOWN)
+        h3q.h3q_timing_enable(False)
+        p = d["p"]
+        per_proj[p.name] = {"gemm_ms": round(g / gn, 4), "lora_down_ms": round(l / ln, 4),
+                            "gemm_tflops": round(2 * S * p.N * (p.K + p.rank) / (g / gn * 1e-3) / 1e12, 1)}
+
+    cpu = None
+    if not args.no_cpu:
+        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(projs, S, args.cpu_rows)
+
+    line = {
+        "metric": "effective TFLOP/s (+% bf16 MFMA peak) of W4+LoRA linear, S=37726",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": "MiniMax-H3 DiT block, four W4+LoRA projections at packed sequence length S",
+                   "S": S, "projections": {p.name: [p.N, p.K, p.rank] for p in wl.BLOCK},
+                   "weights": "NVFP4 (E2M1 + E4M3/16 + fp32)", "lora": "bf16, rank=alpha, strength 1.0",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_w4_kernel<0>", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "avg_launch_ms": round(gemm_avg_ms, 4), "launches": gemm_n,
+                     "flop_per_launch": gemm_flops_launch, "traffic": None},
+        "kernels_ms_per_step": {"gemm": round(gemm_ms / args.steps, 4), "lora_down": round(down_ms / args.steps, 4)},
+        "per_projection": per_proj,
+        "cpu_baseline": cpu,
+    }
+    for d in projs:
+        h3q.h3q_free_weight(d["handle"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,582 @@
+// h3q_api.cpp -- the C ABI of libh3q (declared in include/h3q.h): handles, the resident adapter
+// registry, argument validation, per-stream workspaces and kernel launch sequencing.
+//
+// Per call (FL2VA Turbo, "Implementation" and "Hot API"):
+//   adapter none, or strength 0   -> [prescale x*pqs] -> GEMM over the K base columns only
+//   adapter id                    -> LoRA-down (writes t' and x*pqs) -> GEMM over K + r_pad columns
+//   W4A4 (H3Q_ACT_NVFP4)          -> activation NVFP4 quantizer first; LoRA-down still reads raw x
+// Selecting or switching an adapter is a host-side map lookup: no device work, and the packed
+// weight is never written.
+#include "../../include/h3q.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "h3q_kernels.hpp"
+
+using namespace h3q;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t{1} << 20;
+constexpr int64_t kMaxS = int64_t{1} << 24;
+constexpr int32_t kMaxRank = 512;
+
+thread_local std::string g_error;
+
+h3q_status fail(h3q_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+h3q_status fail(h3q_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+h3q_status ok() {
+  g_error.clear();
+  return H3Q_OK;
+}
+
+#define H3Q_HIP_TRY(expr)                                                                   \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(H3Q_E_HIP, "%s: %s", #expr, hipGetErrorString(e_));   \
+  } while (0)
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- device allocation, with a test hook: while H3Q_TEST_FAIL_ALLOC_AFTER=n is set, the first n
+// allocations after the variable took its current value succeed and every later one fails ----
+std::mutex g_alloc_mu;
+std::string g_alloc_hook;
+long g_alloc_count = 0;
+
+hipError_t dev_alloc(void** p, size_t bytes) {
+  {
+    std::lock_guard<std::mutex> lk(g_alloc_mu);
+    const char* hook = std::getenv("H3Q_TEST_FAIL_ALLOC_AFTER");
+    if (hook) {
+      if (g_alloc_hook != hook) {
+        g_alloc_hook = hook;
+        g_alloc_count = 0;
+      }
+      if (g_alloc_count++ >= std::atol(hook)) return hipErrorOutOfMemory;
+    } else {
+      g_alloc_hook.clear();
+    }
+  }
+  return hipMalloc(p, bytes);
+}
+
+// ---- device check (gfx950 only), cached per device ----
+h3q_status check_device(int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  static std::mutex mu;
+  static std::map<int, bool> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(H3Q_E_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    it = cache.emplace(dev, std::strncmp(prop.gcnArchName, "gfx950", 6) == 0).first;
+  }
+  if (!it->second) return fail(H3Q_E_UNSUPPORTED, "device %d is not gfx950", dev);
+  *dev_out = dev;
+  return H3Q_OK;
+}
+
+// ---- timing ----
+struct TimingRec {
+  int kind;
+  hipEvent_t begin, end;
+};
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimingRec> pending;
+  std::vector<hipEvent_t> pool;
+  double ms[4] = {0, 0, 0, 0};
+  int64_t launches[4] = {0, 0, 0, 0};
+} g_timing;
+
+hipEvent_t take_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launches `fn` on `stream`, bracketed by events of `kind` when timing is on.
+template <class F>
+hipError_t timed(int kind, hipStream_t stream, F&& fn) {
+  TimingRec rec{kind, nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.on) {
+      rec.begin = take_event();
+      rec.end = take_event();
+    }
+  }
+  if (rec.begin && rec.end) {
+    hipError_t e = hipEventRecord(rec.begin, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t err = fn();
+  if (rec.begin && rec.end) {
+    hipError_t e = hipEventRecord(rec.end, stream);
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (e == hipSuccess && err == hipSuccess) {
+      g_timing.pending.push_back(rec);
+    } else {
+      g_timing.pool.push_back(rec.begin);
+      g_timing.pool.push_back(rec.end);
+    }
+    if (err == hipSuccess) err = e;
+  }
+  return err;
+}
+
+// ---- per-(device, stream) grow-only workspace ----
+struct Workspace {
+  void* buf = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+h3q_status workspace(int dev, hipStream_t stream, size_t need, uint8_t** out) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& ws = g_ws[{dev, stream}];
+  if (ws.bytes < need) {
+    if (ws.buf) {
+      H3Q_HIP_TRY(hipStreamSynchronize(stream));  // in-flight work may still read the old buffer
+      H3Q_HIP_TRY(hipFree(ws.buf));
+      ws.buf = nullptr;
+      ws.bytes = 0;
+    }
+    const size_t bytes = static_cast<size_t>(round_up(static_cast<int64_t>(need), int64_t{1} << 21));
+    if (dev_alloc(&ws.buf, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      ws.buf = nullptr;
+      return fail(H3Q_E_NOMEM, "workspace allocation of %zu bytes failed", bytes);
+    }
+    ws.bytes = bytes;
+  }
+  *out = static_cast<uint8_t*>(ws.buf);
+  return H3Q_OK;
+}
+
+}  // namespace
+
+// ---- handles ----
+struct Adapter {
+  int32_t rank = 0, r_pad = 0;
+  float alpha = 0.0f;
+  uint16_t* A = nullptr;  // [r_pad][K_pad]
+  uint16_t* B = nullptr;  // [n_tiles][r_pad/64][256][64]
+};
+
+struct h3q_weight_s {
+  int device = -1;
+  int64_t N = 0, K = 0, K_pad = 0;
+  uint32_t flags = 0;
+  float ts = 1.0f;
+  int32_t n_tiles = 0, k_tiles = 0;
+  uint8_t* codes = nullptr;   // [n_tiles][k_tiles][256][32]
+  uint8_t* scales = nullptr;  // [n_tiles][k_tiles][256][4]
+  size_t codes_bytes = 0, scales_bytes = 0;
+  std::mutex mu;
+  std::map<int32_t, Adapter> adapters;
+};
+
+namespace {
+
+std::mutex g_handles_mu;
+std::unordered_set<h3q_weight> g_handles;
+
+bool live(h3q_weight w) {
+  std::lock_guard<std::mutex> lk(g_handles_mu);
+  return w && g_handles.count(w) != 0;
+}
+
+bool gate_up(const h3q_weight_s* w) { return (w->flags & H3Q_PACK_GATE_UP) != 0; }
+
+void free_adapter(Adapter& a) {
+  if (a.A) (void)hipFree(a.A);
+  if (a.B) (void)hipFree(a.B);
+  a.A = a.B = nullptr;
+}
+
+h3q_status copy_to_device(void** dst, const void* src, size_t bytes) {
+  if (dev_alloc(dst, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    *dst = nullptr;
+    return fail(H3Q_E_NOMEM, "device allocation of %zu bytes failed", bytes);
+  }
+  hipError_t e = hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(*dst);
+    *dst = nullptr;
+    return fail(H3Q_E_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  }
+  return H3Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h3q_last_error(void) { return g_error.c_str(); }
+
+h3q_status h3q_pack_weight(void* stream, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
+                           int64_t N, int64_t K, uint32_t flags, h3q_weight* out) {
+  if (!codes || !scales || !out) return fail(H3Q_E_ARG, "pack: null pointer");
+  if ((flags & ~static_cast<uint32_t>(H3Q_PACK_GATE_UP)) != 0) return fail(H3Q_E_ARG, "pack: unknown flags 0x%x", flags);
+  if (N < 1 || N > kMaxDim || K < 16 || K > kMaxDim || K % 16 != 0)
+    return fail(H3Q_E_SHAPE, "pack: need 1 <= N, K <= 2^20 and K %% 16 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  const bool gu = (flags & H3Q_PACK_GATE_UP) != 0;
+  if (gu && N % 2 != 0) return fail(H3Q_E_SHAPE, "pack: gate/up weight needs an even N (N=%lld)", (long long)N);
+  if (!std::isfinite(tensor_scale) || !(tensor_scale > 0.0f))
+    return fail(H3Q_E_ARG, "pack: tensor_scale must be finite and > 0");
+  for (int64_t i = 0; i < N * (K / 16); ++i)
+    if ((scales[i] & 0x80u) || scales[i] == 0x7Fu)
+      return fail(H3Q_E_FORMAT, "pack: invalid E4M3 scale code 0x%02x at row %lld block %lld", scales[i],
+                  (long long)(i / (K / 16)), (long long)(i % (K / 16)));
+  int dev;
+  if (h3q_status st = check_device(&dev)) return st;
+
+  auto w = new (std::nothrow) h3q_weight_s();
+  if (!w) return fail(H3Q_E_NOMEM, "pack: host allocation failed");
+  w->device = dev;
+  w->N = N;
+  w->K = K;
+  w->K_pad = round_up(K, kGemmBK);
+  w->flags = flags;
+  w->ts = tensor_scale;
+  w->k_tiles = static_cast<int32_t>(w->K_pad / kGemmBK);
+  w->n_tiles = static_cast<int32_t>(gu ? (N / 2 + kGemmBN / 2 - 1) / (kGemmBN / 2) : (N + kGemmBN - 1) / kGemmBN);
+
+  // tile on the host: byte moves only
+  const int64_t prow = static_cast<int64_t>(w->n_tiles) * kGemmBN;
+  std::vector<uint8_t> tc(static_cast<size_t>(prow * w->k_tiles * kCodeBytesPerRowTile), 0);
+  std::vector<uint8_t> tsc(static_cast<size_t>(prow * w->k_tiles * kScaleBytesPerRowTile), 0);
+  for (int64_t nt = 0; nt < w->n_tiles; ++nt)
+    for (int64_t c = 0; c < kGemmBN; ++c) {
+      const int64_t n = packed_row_source(nt, c, gu, N);
+      if (n < 0) continue;
+      for (int64_t kt = 0; kt < w->k_tiles; ++kt) {
+        const int64_t tile_row = (nt * w->k_tiles + kt) * kGemmBN + c;
+        const int64_t cb = std::min<int64_t>(kCodeBytesPerRowTile, K / 2 - kt * kCodeBytesPerRowTile);
+        const int64_t sb = std::min<int64_t>(kScaleBytesPerRowTile, K / 16 - kt * kScaleBytesPerRowTile);
+        std::memcpy(&tc[tile_row * kCodeBytesPerRowTile], codes + n * (K / 2) + kt * kCodeBytesPerRowTile, cb);
+        std::memcpy(&tsc[tile_row * kScaleBytesPerRowTile], scales + n * (K / 16) + kt * kScaleBytesPerRowTile, sb);
+      }
+    }
+  w->codes_bytes = tc.size();
+  w->scales_bytes = tsc.size();
+  (void)stream;  // synchronous copies: the caller's buffers are host memory
+  h3q_status st = copy_to_device(reinterpret_cast<void**>(&w->codes), tc.data(), tc.size());
+  if (st == H3Q_OK) st = copy_to_device(reinterpret_cast<void**>(&w->scales), tsc.data(), tsc.size());
+  if (st != H3Q_OK) {
+    if (w->codes) (void)hipFree(w->codes);
+    delete w;
+    return st;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_handles_mu);
+    g_handles.insert(w);
+  }
+  *out = w;
+  return ok();
+}
+
+h3q_status h3q_free_weight(h3q_weight w) {
+  {
+    std::lock_guard<std::mutex> lk(g_handles_mu);
+    if (!w || g_handles.erase(w) == 0) return fail(H3Q_E_ARG, "free: not a live weight handle");
+  }
+  for (auto& kv : w->adapters) free_adapter(kv.second);
+  (void)hipFree(w->codes);
+  (void)hipFree(w->scales);
+  delete w;
+  return ok();
+}
+
+h3q_status h3q_weight_info(h3q_weight w, int64_t* N, int64_t* K, uint32_t* flags) {
+  if (!live(w)) return fail(H3Q_E_ARG, "weight_info: not a live weight handle");
+  if (N) *N = w->N;
+  if (K) *K = w->K;
+  if (flags) *flags = w->flags;
+  return ok();
+}
+
+h3q_status h3q_register_adapter(h3q_weight w, int32_t id, const uint16_t* A, const uint16_t* B, int32_t rank,
+                                float alpha) {
+  if (!live(w)) return fail(H3Q_E_ARG, "register_adapter: not a live weight handle");
+  if (!A || !B) return fail(H3Q_E_ARG, "register_adapter: null A or B");
+  if (id < 0) return fail(H3Q_E_ADAPTER, "register_adapter: id must be >= 0 (got %d)", id);
+  if (rank < 1 || rank > kMaxRank) return fail(H3Q_E_SHAPE, "register_adapter: rank must be in [1, %d] (got %d)", kMaxRank, rank);
+  if (!std::isfinite(alpha)) return fail(H3Q_E_ARG, "register_adapter: alpha must be finite");
+  std::lock_guard<std::mutex> lk(w->mu);
+  if (w->adapters.count(id)) return fail(H3Q_E_ADAPTER, "register_adapter: id %d already registered", id);
+  int dev;
+  if (h3q_status st = check_device(&dev)) return st;
+  if (dev != w->device) return fail(H3Q_E_ARG, "register_adapter: weight lives on device %d, current is %d", w->device, dev);
+
+  Adapter a;
+  a.rank = rank;
+  a.r_pad = static_cast<int32_t>(round_up(rank, 64));
+  a.alpha = alpha;
+  const int64_t K = w->K, Kp = w->K_pad, N = w->N;
+  std::vector<uint16_t> Ah(static_cast<size_t>(a.r_pad * Kp), 0);
+  for (int64_t j = 0; j < rank; ++j) std::memcpy(&Ah[j * Kp], A + j * K, K * sizeof(uint16_t));
+  const int64_t r_tiles = a.r_pad / 64;
+  std::vector<uint16_t> Bh(static_cast<size_t>(int64_t{w->n_tiles} * r_tiles * kGemmBN * 64), 0);
+  for (int64_t nt = 0; nt < w->n_tiles; ++nt)
+    for (int64_t c = 0; c < kGemmBN; ++c) {
+      const int64_t n = packed_row_source(nt, c, gate_up(w), N);
+      if (n < 0) continue;
+      for (int64_t j = 0; j < rank; ++j)
+        Bh[((nt * r_tiles + j / 64) * kGemmBN + c) * 64 + j % 64] = B[n * rank + j];
+    }
+  h3q_status st = copy_to_device(reinterpret_cast<void**>(&a.A), Ah.data(), Ah.size() * 2);
+  if (st == H3Q_OK) st = copy_to_device(reinterpret_cast<void**>(&a.B), Bh.data(), Bh.size() * 2);
+  if (st != H3Q_OK) {
+    free_adapter(a);
+    return st;
+  }
+  w->adapters.emplace(id, a);
+  return ok();
+}
+
+h3q_status h3q_unregister_adapter(h3q_weight w, int32_t id) {
+  if (!live(w)) return fail(H3Q_E_ARG, "unregister_adapter: not a live weight handle");
+  std::lock_guard<std::mutex> lk(w->mu);
+  auto it = w->adapters.find(id);
+  if (it == w->adapters.end()) return fail(H3Q_E_ADAPTER, "unregister_adapter: unknown id %d", id);
+  free_adapter(it->second);
+  w->adapters.erase(it);
+  return ok();
+}
+
+h3q_status h3q_list_adapters(h3q_weight w, int32_t* ids, int32_t cap, int32_t* count) {
+  if (!live(w)) return fail(H3Q_E_ARG, "list_adapters: not a live weight handle");
+  if (!count || (cap > 0 && !ids)) return fail(H3Q_E_ARG, "list_adapters: null pointer");
+  std::lock_guard<std::mutex> lk(w->mu);
+  int32_t i = 0;
+  for (auto& kv : w->adapters) {
+    if (i < cap) ids[i] = kv.first;
+    ++i;
+  }
+  *count = i;
+  return ok();
+}
+
+h3q_status h3q_linear_ex(void* stream_, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                         int32_t adapter_id, float strength, uint32_t flags, uint16_t* out) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!live(w)) return fail(H3Q_E_ARG, "linear: not a live weight handle");
+  if (S != 0 && (!x || !out)) return fail(H3Q_E_ARG, "linear: null x or output");
+  if ((flags & ~static_cast<uint32_t>(H3Q_ACT_NVFP4 | H3Q_EPI_SWIGLU)) != 0)
+    return fail(H3Q_E_ARG, "linear: unknown flags 0x%x", flags);
+  if (S < 0 || S > kMaxS) return fail(H3Q_E_SHAPE, "linear: S must be in [0, 2^24] (got %lld)", (long long)S);
+  if (!std::isfinite(strength)) return fail(H3Q_E_ARG, "linear: strength must be finite");
+  const bool swiglu = (flags & H3Q_EPI_SWIGLU) != 0;
+  const bool w4a4 = (flags & H3Q_ACT_NVFP4) != 0;
+  if (swiglu && !gate_up(w)) return fail(H3Q_E_ARG, "linear: SwiGLU output needs a weight packed with H3Q_PACK_GATE_UP");
+  if (!aligned16(x) || (pqs && !aligned16(pqs)))
+    return fail(H3Q_E_ARG, "linear: x and pqs must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(out) & 1u) != 0) return fail(H3Q_E_ARG, "linear: output must be 2-byte aligned");
+  const int64_t n_out = swiglu ? w->N / 2 : w->N;
+  {
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), xe = xb + static_cast<uintptr_t>(S * w->K * 2);
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(out), oe = ob + static_cast<uintptr_t>(S * n_out * 2);
+    if (S > 0 && xb < oe && ob < xe) return fail(H3Q_E_ARG, "linear: output overlaps x");
+  }
+
+  std::unique_lock<std::mutex> lk(w->mu);
+  const Adapter* ad = nullptr;
+  if (adapter_id != H3Q_ADAPTER_NONE) {
+    auto it = w->adapters.find(adapter_id);
+    if (it == w->adapters.end()) return fail(H3Q_E_ADAPTER, "linear: unknown adapter id %d", adapter_id);
+    ad = &it->second;
+  }
+  const bool lora = ad != nullptr && strength != 0.0f;
+  float f = 0.0f;
+  if (lora) {
+    const double fd = static_cast<double>(strength) * ad->alpha / (static_cast<double>(ad->rank) * w->ts);
+    f = static_cast<float>(fd);
+    if (!std::isfinite(f)) return fail(H3Q_E_ARG, "linear: strength*alpha/(rank*tensor_scale) overflows fp32");
+  }
+  if (S == 0) return ok();
+
+  int dev = -1;
+  H3Q_HIP_TRY(hipGetDevice(&dev));
+  if (dev != w->device) return fail(H3Q_E_ARG, "linear: weight lives on device %d, current is %d", w->device, dev);
+
+  // workspace: [amax/ts_a : 256 B][act operand: S x K_pad bf16][t': S x r_pad bf16]
+  const bool direct_x = !w4a4 && !pqs && w->K == w->K_pad;  // x itself is the GEMM operand
+  const size_t small = 256;
+  const size_t act_bytes = direct_x ? 0 : static_cast<size_t>(round_up(S * w->K_pad * 2, 256));
+  const size_t t_bytes = lora ? static_cast<size_t>(round_up(S * ad->r_pad * 2, 256)) : 0;
+  uint8_t* ws = nullptr;
+  if (h3q_status st = workspace(dev, stream, small + act_bytes + t_bytes, &ws)) return st;
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(ws);
+  float* ts_a = reinterpret_cast<float*>(ws + 4);
+  uint16_t* act = direct_x ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(ws + small);
+  uint16_t* tbuf = lora ? reinterpret_cast<uint16_t*>(ws + small + act_bytes) : nullptr;
+
+  hipError_t e = hipSuccess;
+  if (w4a4) {
+    ActQuantParams q{x, pqs, S, w->K, amax_bits, ts_a, nullptr, nullptr, act, w->K_pad};
+    e = timed(H3Q_KERNEL_ACT_QUANT, stream, [&] { return launch_act_quant(q, stream); });
+    if (e != hipSuccess) return fail(H3Q_E_HIP, "act-quant launch: %s", hipGetErrorString(e));
+  }
+  if (lora) {
+    LoraDownParams lp{x, pqs, ad->A, S, w->K, w->K_pad, ad->r_pad, f, w4a4 ? ts_a : nullptr, tbuf,
+                      (w4a4 || direct_x) ? nullptr : act};
+    e = timed(H3Q_KERNEL_LORA_DOWN, stream, [&] { return launch_lora_down(lp, stream); });
+    if (e != hipSuccess) return fail(H3Q_E_HIP, "lora-down launch: %s", hipGetErrorString(e));
+  } else if (!w4a4 && !direct_x) {
+    PrescaleParams pp{x, pqs, S, w->K, w->K_pad, act};
+    e = timed(H3Q_KERNEL_PRESCALE, stream, [&] { return launch_prescale(pp, stream); });
+    if (e != hipSuccess) return fail(H3Q_E_HIP, "prescale launch: %s", hipGetErrorString(e));
+  }
+  GemmParams g{};
+  g.act = act;
+  g.act_ld = direct_x ? w->K : w->K_pad;
+  g.lora_t = tbuf;
+  g.lora_t_ld = lora ? ad->r_pad : 0;
+  g.wcodes = w->codes;
+  g.wscales = w->scales;
+  g.lora_b = lora ? ad->B : nullptr;
+  g.S = S;
+  g.k_tiles = w->k_tiles;
+  g.r_tiles = lora ? ad->r_pad / 64 : 0;
+  g.m_tiles = static_cast<int32_t>((S + kGemmBM - 1) / kGemmBM);
+  g.n_tiles = w->n_tiles;
+  g.n_out = n_out;
+  g.gate_up = gate_up(w) ? 1 : 0;
+  g.ts = w->ts;
+  g.ts_dev = w4a4 ? ts_a : nullptr;
+  g.out = out;
+  g.out_ld = n_out;
+  e = timed(H3Q_KERNEL_GEMM, stream,
+            [&] { return launch_gemm_w4(g, swiglu ? Epilogue::SwiGLU : Epilogue::Plain, stream); });
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+h3q_status h3q_linear(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                      int32_t adapter_id, float strength, uint16_t* y) {
+  return h3q_linear_ex(stream, x, S, pqs, w, adapter_id, strength, 0u, y);
+}
+
+h3q_status h3q_linear_swiglu(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                             int32_t adapter_id, float strength, uint16_t* h) {
+  return h3q_linear_ex(stream, x, S, pqs, w, adapter_id, strength, H3Q_EPI_SWIGLU, h);
+}
+
+h3q_status h3q_quantize_nvfp4(void* stream_, const uint16_t* x, int64_t S, int64_t K, const float* pqs,
+                              uint8_t* codes, uint8_t* scales, float* ts) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!x || !codes || !scales || !ts) return fail(H3Q_E_ARG, "quantize_nvfp4: null pointer");
+  if (S < 0 || S > kMaxS || K < 16 || K > kMaxDim || K % 16 != 0)
+    return fail(H3Q_E_SHAPE, "quantize_nvfp4: need 0 <= S <= 2^24, 16 <= K <= 2^20, K %% 16 == 0");
+  if (!aligned16(x) || (pqs && !aligned16(pqs)) || (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return fail(H3Q_E_ARG, "quantize_nvfp4: x, pqs must be 16-byte and codes 8-byte aligned");
+  int dev;
+  if (h3q_status st = check_device(&dev)) return st;
+  uint8_t* ws = nullptr;
+  if (h3q_status st = workspace(dev, stream, 256, &ws)) return st;
+  ActQuantParams q{x, pqs, S, K, reinterpret_cast<uint32_t*>(ws), ts, codes, scales, nullptr, K};
+  hipError_t e = timed(H3Q_KERNEL_ACT_QUANT, stream, [&] { return launch_act_quant(q, stream); });
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "act-quant launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+h3q_status h3q_debug_dequant(void* stream, h3q_weight w, uint16_t* wq) {
+  if (!live(w)) return fail(H3Q_E_ARG, "debug_dequant: not a live weight handle");
+  if (!wq || !aligned16(wq)) return fail(H3Q_E_ARG, "debug_dequant: output must be non-null and 16-byte aligned");
+  DequantParams p{w->codes, w->scales, w->n_tiles, w->k_tiles, gate_up(w), w->N, w->K, wq};
+  hipError_t e = launch_debug_dequant(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "debug_dequant launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+h3q_status h3q_weight_checksum(void* stream, h3q_weight w, uint64_t* out) {
+  if (!live(w)) return fail(H3Q_E_ARG, "weight_checksum: not a live weight handle");
+  if (!out) return fail(H3Q_E_ARG, "weight_checksum: null output");
+  H3Q_HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  std::vector<uint8_t> host(w->codes_bytes + w->scales_bytes);
+  H3Q_HIP_TRY(hipMemcpy(host.data(), w->codes, w->codes_bytes, hipMemcpyDeviceToHost));
+  H3Q_HIP_TRY(hipMemcpy(host.data() + w->codes_bytes, w->scales, w->scales_bytes, hipMemcpyDeviceToHost));
+  uint64_t h = 1469598103934665603ull;  // FNV-1a 64
+  for (uint8_t b : host) {
+    h ^= b;
+    h *= 1099511628211ull;
+  }
+  *out = h;
+  return ok();
+}
+
+h3q_status h3q_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  for (auto& r : g_timing.pending) {
+    (void)hipEventSynchronize(r.end);
+    g_timing.pool.push_back(r.begin);
+    g_timing.pool.push_back(r.end);
+  }
+  g_timing.pending.clear();
+  for (int k = 0; k < 4; ++k) {
+    g_timing.ms[k] = 0.0;
+    g_timing.launches[k] = 0;
+  }
+  return ok();
+}
+
+h3q_status h3q_timing_get(int32_t kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind > 3 || !total_ms || !launches) return fail(H3Q_E_ARG, "timing_get: bad kind or null pointer");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& r : g_timing.pending) {
+    float ms = 0.0f;
+    H3Q_HIP_TRY(hipEventSynchronize(r.end));
+    H3Q_HIP_TRY(hipEventElapsedTime(&ms, r.begin, r.end));
+    g_timing.ms[r.kind] += ms;
+    g_timing.launches[r.kind] += 1;
+    g_timing.pool.push_back(r.begin);
+    g_timing.pool.push_back(r.end);
+  }
+  g_timing.pending.clear();
+  *total_ms = g_timing.ms[kind];
+  *launches = g_timing.launches[kind];
+  g_timing.ms[kind] = 0.0;
+  g_timing.launches[kind] = 0;
+  return ok();
+}
+
+}  // extern "C"

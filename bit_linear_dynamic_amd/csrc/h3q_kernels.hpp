@@ -1,0 +1,103 @@
+// h3q_kernels.hpp -- launch interface between the C-ABI layer (h3q_api.cpp) and the gfx950 kernels.
+// Host-side only: parameter blocks and launcher functions; every launcher returns the HIP error of
+// its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3q {
+
+// Tile geometry of the main GEMM and of the packed weight layout (see gemm_w4.hip).
+constexpr int kGemmBM = 256;   // rows of x per workgroup tile
+constexpr int kGemmBN = 256;   // output columns (packed weight rows) per workgroup tile
+constexpr int kGemmBK = 64;    // K per pipeline stage
+constexpr int kCodeBytesPerRowTile = kGemmBK / 2;   // 32 bytes of E2M1 codes per row per K-tile
+constexpr int kScaleBytesPerRowTile = kGemmBK / 16; // 4 E4M3 scales per row per K-tile
+
+struct GemmParams {
+  const uint16_t* act;      // bf16 [S][act_ld]: activation operand (x, x*pqs, or decoded NVFP4 x)
+  int64_t act_ld;
+  const uint16_t* lora_t;   // bf16 [S][r_pad]: f * (A x), folded in as extra K-columns; or null
+  int64_t lora_t_ld;
+  const uint8_t* wcodes;    // [n_tiles][k_tiles][256][32]
+  const uint8_t* wscales;   // [n_tiles][k_tiles][256][4]
+  const uint16_t* lora_b;   // bf16 [n_tiles][r_tiles][256][64], rows in the weight's tile order
+  int64_t S;
+  int32_t k_tiles;          // K_pad / 64
+  int32_t r_tiles;          // r_pad / 64 (0: no adapter)
+  int32_t m_tiles, n_tiles;
+  int64_t n_out;            // valid output columns (N, or N/2 for SwiGLU)
+  int32_t gate_up;          // weight packed with interleaved gate/up column tiles
+  float ts;                 // weight tensor scale
+  const float* ts_dev;      // optional device scalar multiplying ts (W4A4 activation scale)
+  uint16_t* out;            // bf16 [S][n_out]
+  int64_t out_ld;
+};
+
+enum class Epilogue { Plain = 0, SwiGLU = 1 };
+
+hipError_t launch_gemm_w4(const GemmParams& p, Epilogue epi, hipStream_t stream);
+size_t gemm_w4_lds_bytes();
+
+struct LoraDownParams {
+  const uint16_t* x;        // bf16 [S][K] (caller's activation)
+  const float* pqs;         // fp32 [K] or null
+  const uint16_t* A;        // bf16 [r_pad][K_pad], zero padded
+  int64_t S, K, K_pad;
+  int32_t r_pad;
+  float f;                  // t' = bf16(f / (*f_div_dev or 1) * (A x))
+  const float* f_div_dev;
+  uint16_t* t_out;          // bf16 [S][r_pad]
+  uint16_t* xs_out;         // bf16 [S][K_pad] = x * pqs, or null
+};
+constexpr int kLoraBM = 128;
+hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream);
+
+struct PrescaleParams {
+  const uint16_t* x;        // bf16 [S][K]
+  const float* pqs;         // fp32 [K] or null
+  int64_t S, K, K_pad;
+  uint16_t* xs_out;         // bf16 [S][K_pad]
+};
+hipError_t launch_prescale(const PrescaleParams& p, hipStream_t stream);
+
+struct ActQuantParams {
+  const uint16_t* x;        // bf16 [S][K]
+  const float* pqs;         // fp32 [K] or null
+  int64_t S, K;
+  uint32_t* amax_bits;      // device scratch: global amax as fp32 bits
+  float* ts_out;            // device fp32 [1]
+  uint8_t* codes;           // [S][K/2] or null
+  uint8_t* scales;          // [S][K/16] or null
+  uint16_t* xq_out;         // bf16 [S][xq_ld] = E2M1 * E4M3 (no ts), or null
+  int64_t xq_ld;            // >= K; columns [K, xq_ld) are written as zero
+};
+hipError_t launch_act_quant(const ActQuantParams& p, hipStream_t stream);
+
+// Row of the caller's weight that row c of packed column tile nt holds, or -1 for padding.
+// Plain: nt*256 + c. Gate/up (F = N/2): the tile interleaves 32-row groups of gate rows
+// nt*128 + (c/64)*32 + c%32 and the matching up rows F + (same), so that one workgroup holds both
+// halves of every output column of SiLU(gate) * up.
+__host__ __device__ inline int64_t packed_row_source(int64_t nt, int64_t c, bool gate_up, int64_t N) {
+  if (!gate_up) {
+    const int64_t n = nt * kGemmBN + c;
+    return n < N ? n : -1;
+  }
+  const int64_t F = N / 2;
+  const int64_t j = nt * (kGemmBN / 2) + (c / 64) * 32 + (c % 32);
+  if (j >= F) return -1;
+  return ((c / 32) % 2) ? F + j : j;
+}
+
+struct DequantParams {
+  const uint8_t* wcodes;
+  const uint8_t* wscales;
+  int32_t n_tiles, k_tiles;
+  bool gate_up;
+  int64_t N, K;
+  uint16_t* out;            // bf16 [N][K]
+};
+hipError_t launch_debug_dequant(const DequantParams& p, hipStream_t stream);
+
+}  // namespace h3q

@@ -1,0 +1,153 @@
+/* h3q.h -- C ABI of the MI355X (gfx950) W4 + dynamic LoRA linear.
+ *
+ * The operation (FL2VA Turbo page, section "Implementation"):
+ *
+ *     y = NVFP4_base(x (*) pre_quant_scale) + strength * (alpha / rank) * B(A x)
+ *
+ *   - the base weight W [N][K] is NVFP4: E2M1 element codes, one E4M3 ("FN": bias 7, no inf,
+ *     NaN = 0x7F/0xFF) scale per 16 consecutive K-elements, and one fp32 tensor scale that
+ *     multiplies on decode (the pages name only "NVFP4"; the layout below is this library's);
+ *   - pre_quant_scale (pqs) multiplies the activation on the base path only; the bf16 LoRA branch
+ *     receives the original activation (same section);
+ *   - adapters stay resident and are selected per call; the LoRA delta is never merged into the
+ *     packed weight, which no call ever writes (FL2VA Turbo, opening paragraph and "Hot API":
+ *     "none" selects the base path);
+ *   - fused QKV and fused gate/up are single matrices; gate/up output may be reduced in the same
+ *     call to SiLU(gate) * up (MiniMax-H3 Ultra Fast, "Active optimization stack", MLP row, and
+ *     "Kernel path");
+ *   - W4A4 variant: the base path's activation is itself quantized to NVFP4 on every call
+ *     (MiniMax-H3 Ultra Fast, "Kernel path", item 1).
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns; all 2-D arrays are row-major and dense.
+ *   - "host" pointers are read before the call returns; "device" pointers must stay valid until
+ *     the work enqueued on `stream` (a hipStream_t; NULL = the null stream) has run.
+ *   - every call returns H3Q_OK (0) or a positive H3Q_E_* code; on error nothing has been enqueued,
+ *     no output has been written, and h3q_last_error() describes the failure.
+ *   - a weight handle belongs to the device that was current when it was packed; calls that use it
+ *     must be made with that device current.
+ *   - calls on different streams may run concurrently; registering or unregistering an adapter
+ *     while a call that uses the same handle is in flight is not allowed.
+ */
+#ifndef H3Q_H
+#define H3Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t h3q_status;
+typedef struct h3q_weight_s* h3q_weight; /* opaque; owns its device memory */
+
+enum {
+  H3Q_OK = 0,
+  H3Q_E_ARG = 1,         /* null pointer, non-finite scalar, bad flag */
+  H3Q_E_SHAPE = 2,       /* dimensions out of range or inconsistent */
+  H3Q_E_FORMAT = 3,      /* invalid NVFP4 scale code (sign bit set or NaN) */
+  H3Q_E_ADAPTER = 4,     /* unknown or duplicate adapter id */
+  H3Q_E_NOMEM = 5,       /* device or host allocation failed */
+  H3Q_E_HIP = 6,         /* HIP runtime error (message carries hipGetErrorString) */
+  H3Q_E_UNSUPPORTED = 7  /* current device is not gfx950 */
+};
+
+#define H3Q_ADAPTER_NONE (-1)
+
+/* h3q_pack_weight flags */
+enum { H3Q_PACK_GATE_UP = 1u << 0 }; /* rows [0, N/2) are gate, [N/2, N) are up (N even) */
+
+/* h3q_linear_ex flags */
+enum {
+  H3Q_ACT_NVFP4 = 1u << 0,  /* W4A4: quantize x (*) pqs to NVFP4 per call for the base path */
+  H3Q_EPI_SWIGLU = 1u << 1  /* output SiLU(gate) * up, [S][N/2]; needs an H3Q_PACK_GATE_UP weight */
+};
+
+/* Limits: 1 <= N, K <= 2^20 with K % 16 == 0 (and N even for H3Q_PACK_GATE_UP);
+ * 1 <= rank <= 512; 0 <= S <= 2^24. */
+
+/* Pack an NVFP4 weight (FL2VA Turbo, opening paragraph: the packed base that adapters are switched
+ * over without rebuilding).
+ *   codes  host  uint8 [N][K/2]  E2M1 codes, element k in the low nibble of byte k/2 when k is even
+ *   scales host  uint8 [N][K/16] E4M3FN block scales; codes with the sign bit set or 0x7F -> E_FORMAT
+ *   tensor_scale  fp32 > 0, finite; the decoded weight is E2M1 * E4M3 * tensor_scale
+ * Copies into a device layout tiled for the GEMM (byte moves only; the values are untouched),
+ * synchronizes `stream`, and returns a handle in *out. The caller may free codes/scales after. */
+h3q_status h3q_pack_weight(void* stream, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
+                           int64_t N, int64_t K, uint32_t flags, h3q_weight* out);
+
+/* Release a handle and every adapter registered on it (no call using it may be in flight). */
+h3q_status h3q_free_weight(h3q_weight w);
+
+/* Register a resident LoRA adapter on one projection (FL2VA Turbo, "Implementation": A, B, rank and
+ * alpha per target, validated at load).
+ *   id     >= 0, unique on this handle (else E_ADAPTER); ids are scoped per handle
+ *   A      host  bf16 [rank][K];   B  host  bf16 [N][rank];   alpha finite
+ * Copies to device memory and synchronizes; the caller may free A and B after. */
+h3q_status h3q_register_adapter(h3q_weight w, int32_t id, const uint16_t* A, const uint16_t* B, int32_t rank,
+                                float alpha);
+
+/* Drop an adapter (E_ADAPTER if unknown). No call using it may be in flight. */
+h3q_status h3q_unregister_adapter(h3q_weight w, int32_t id);
+
+/* Registered ids of a handle: writes up to `cap` ids to `ids` (host) and the total to *count. */
+h3q_status h3q_list_adapters(h3q_weight w, int32_t* ids, int32_t cap, int32_t* count);
+
+/* Dimensions and flags of a handle (any out-pointer may be NULL). */
+h3q_status h3q_weight_info(h3q_weight w, int64_t* N, int64_t* K, uint32_t* flags);
+
+/* The projection (FL2VA Turbo, "Implementation"):
+ *   x    device bf16 [S][K]     the original activation
+ *   pqs  device fp32 [K]        pre_quant_scale of the base path, or NULL for all ones
+ *   adapter_id                  a registered id, or H3Q_ADAPTER_NONE for the base path
+ *   strength                    finite; 0 runs the base path (bit-identical to adapter none)
+ *   y    device bf16 [S][N]     every element written; must not overlap x
+ * Asynchronous on `stream`. S == 0 is a no-op. */
+h3q_status h3q_linear(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                      int32_t adapter_id, float strength, uint16_t* y);
+
+/* Fused gate/up projection followed by SiLU(gate) * up (MiniMax-H3 Ultra Fast, "Kernel path"):
+ * w must be packed with H3Q_PACK_GATE_UP; h device bf16 [S][N/2]. Otherwise as h3q_linear. */
+h3q_status h3q_linear_swiglu(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                             int32_t adapter_id, float strength, uint16_t* h);
+
+/* h3q_linear with flags (H3Q_ACT_NVFP4, H3Q_EPI_SWIGLU). out is [S][N] or, with H3Q_EPI_SWIGLU,
+ * [S][N/2]. With H3Q_ACT_NVFP4 the LoRA branch still receives the original bf16 x. */
+h3q_status h3q_linear_ex(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                         int32_t adapter_id, float strength, uint32_t flags, uint16_t* out);
+
+/* The W4A4 activation quantizer on its own (MiniMax-H3 Ultra Fast, "Kernel path", item 1), as
+ * h3q_linear_ex(H3Q_ACT_NVFP4) runs it:
+ *   v      = f32(x) * pqs[k] rounded to fp32            (pqs NULL -> v = x)
+ *   ts     = amax|v| / (6 * 448) rounded to fp32         (1 when v is all zero)
+ *   scale  = E4M3 nearest to amax_block|v| / (6 * ts), ties to even, saturating at 448
+ *   code   = E2M1 nearest to v / (E4M3(scale) * ts), ties to even, saturating at 6; 0 if scale is 0
+ * Each quotient is the exact quotient rounded once. All pointers are device pointers:
+ *   x bf16 [S][K], pqs fp32 [K] or NULL, codes uint8 [S][K/2], scales uint8 [S][K/16], ts fp32 [1].
+ * K % 16 == 0. Asynchronous on `stream`. */
+h3q_status h3q_quantize_nvfp4(void* stream, const uint16_t* x, int64_t S, int64_t K, const float* pqs,
+                              uint8_t* codes, uint8_t* scales, float* ts);
+
+/* Diagnostic: the weight as the GEMM's decode stage sees it, E2M1 * E4M3 without the tensor scale
+ * (exact in bf16), written to device bf16 [N][K]. Uses the same device decode as the GEMM. */
+h3q_status h3q_debug_dequant(void* stream, h3q_weight w, uint16_t* wq);
+
+/* Diagnostic: 64-bit FNV-1a hash of the packed weight's device bytes (synchronizes `stream`).
+ * Unchanged across any number of h3q_linear calls: the packed base is never written. */
+h3q_status h3q_weight_checksum(void* stream, h3q_weight w, uint64_t* out);
+
+/* Kernel timing with HIP events recorded on the call's stream around each launch of one kind.
+ * Off by default. h3q_timing_get waits for the recorded events, returns the summed milliseconds
+ * and the number of launches of `kind` since the last get (or enable), and resets that kind. */
+enum { H3Q_KERNEL_GEMM = 0, H3Q_KERNEL_LORA_DOWN = 1, H3Q_KERNEL_PRESCALE = 2, H3Q_KERNEL_ACT_QUANT = 3 };
+h3q_status h3q_timing_enable(int32_t on);
+h3q_status h3q_timing_get(int32_t kind, double* total_ms, int64_t* launches);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* h3q_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3Q_H */

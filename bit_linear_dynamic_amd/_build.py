@@ -13,6 +13,10 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3q.so")
 
 SOURCES = ["h3q_api.cpp", "gemm_w4.hip", "lora_down.hip", "act_quant.hip", "misc.hip"]
+# The GEMM-shaped kernels are scheduled for instruction-level parallelism rather than register
+# pressure: they run one wave per SIMD anyway, and this lets LDS operand reads run ahead of the MFMAs.
+PER_FILE = {"gemm_w4.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+            "lora_down.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops (v_pk_*_f32).
@@ -24,7 +28,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *PER_FILE.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

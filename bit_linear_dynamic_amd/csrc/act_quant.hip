@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActQuantParams p) {
       amax_b = fmaxf(amax_b, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
     }
     const uint32_t sc = e4m3_rne_satfinite(static_cast<double>(amax_b) / six_ts);
-    const float s = e4m3_to_f32(sc);
+    const float s = e4m3_byte_to_f32<0>(sc);
     const double d = static_cast<double>(s) * static_cast<double>(ts);  // exact
     uint32_t cw[2] = {0u, 0u};
 #pragma unroll
@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActQuantParams p) {
     if (p.scales) p.scales[row * blocks_per_row + k0 / 16] = static_cast<uint8_t>(sc);
     if (p.xq_out) {
       uint16_t* dst = p.xq_out + row * p.xq_ld + k0;
-      *reinterpret_cast<u32x4*>(dst) = nvfp4_word_to_bf16x8(cw[0], s);
-      *reinterpret_cast<u32x4*>(dst + 8) = nvfp4_word_to_bf16x8(cw[1], s);
+      *reinterpret_cast<u32x4*>(dst) = nvfp4_dword_to_bf16x8(cw[0], s);
+      *reinterpret_cast<u32x4*>(dst + 8) = nvfp4_dword_to_bf16x8(cw[1], s);
     }
   }
   // zero the K padding of the decoded operand, if any

@@ -5,26 +5,28 @@
 //   h[s][j]   = bf16( SiLU(ts*acc[s][j]) * ts*acc[s][F+j] )  (gate/up epilogue)
 //
 // The base term is the NVFP4 projection of FL2VA Turbo, "Implementation"; Wq = E2M1 * E4M3 is
-// decoded into LDS as exact bf16. The LoRA-up is folded into the same accumulator as r_pad extra
-// K-columns (the concatenation identity W u + B (A s) = [W | B] [u ; A s] of the MiniMax-H3 Turbo
-// CMF card, "What the conversion did"), with t' = strength*alpha/(rank*ts) * (A x) so that one
-// scale by ts finishes both terms. The gate/up epilogue is the in-place SiLU x up of MiniMax-H3
-// Ultra Fast, "Kernel path".
+// exact in bf16, so it is decoded without rounding and fed to bf16 matrix cores. The LoRA-up is
+// folded into the same accumulator as r_pad extra K-columns (the concatenation identity
+// W u + B (A s) = [W | B] [u ; A s] of the MiniMax-H3 Turbo CMF card, "What the conversion did"),
+// with t' = strength*alpha/(rank*ts) * (A x) so that one scale by ts finishes both terms. The gate/up
+// epilogue is the in-place SiLU x up of MiniMax-H3 Ultra Fast, "Kernel path".
 //
-// Geometry: 256 threads (4 wave64s in a 2x2 grid), a 256x256 output tile per workgroup, K staged
-// 64 at a time through double-buffered LDS (2 x (32 KiB activation + 32 KiB weight)); each wave owns
-// a 128x128 quarter as 4x4 tiles of v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Rows past S
-// are computed from a clamped (repeated) input row and never stored.
+// Geometry: 256 threads = 4 wave64s side by side (1 x 4), a 256 x 256 output tile per workgroup;
+// wave w owns all 256 rows and columns [64w, 64w+64) as 8 x 2 tiles of v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators. K is staged 64 at a time through two LDS stages of 64 KiB:
+//   activation  256 rows x 64 bf16, 16-byte chunks XOR-swizzled by (row/2)%8        32 KiB
+//   weight      W4 K-tile: 8 runs of 256 code dwords (+32 dwords padding each), then 256 scale
+//               dwords (9 KiB + 1 KiB); or, for a LoRA K-tile, 256 rows x 64 bf16 of B  32 KiB
+// Every global->LDS copy is a buffer_load ... lds (16 bytes per lane, no registers, out-of-range
+// offsets read as zero). The weight stays 4-bit in LDS: each wave decodes the B operand of its own 64
+// columns straight into MFMA registers -- one code dword (8 consecutive k of one column) and one
+// E4M3 scale per lane per 32x32x16 step -- so no column is decoded twice and no bf16 weight tile is
+// written to LDS. Rows past S lie outside the activation buffer, load as zero and are never stored.
 //
-// Weight layout (written by h3q_pack_weight): for tile column block nt and K-tile kt, the 256 rows'
-// 32 code bytes are contiguous ([nt][kt][256][32]) and so are their 4 scale bytes ([nt][kt][256][4]);
-// one thread loads and decodes one row. The LoRA B factor is stored the same way in bf16
-// ([nt][rt][256][64]).
-//
-// Workgroup -> tile order: the hardware hands workgroup b to XCD b % 8. Work item w is mapped so
-// that each XCD walks a contiguous range of the (M-tile major, N-tile minor) order: the ~32
-// workgroups resident on one XCD then share one activation M-tile in that XCD's L2 while they
-// stream different weight tiles.
+// Workgroup -> tile order: the hardware hands workgroup b to XCD b % 8; work item w is mapped so that
+// each XCD walks a contiguous range of the (M-tile major, N-tile minor) order, so the workgroups
+// resident on one XCD share one activation M-tile in that XCD's L2 while streaming weight tiles.
+#include <algorithm>
 #include <mutex>
 
 #include "h3q_device.hpp"
@@ -36,160 +38,247 @@ namespace {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
 constexpr int kThreads = 256;
-constexpr uint32_t kTileBytes = BM * BK * 2;            // 32 KiB per operand per stage
-constexpr uint32_t kStageBytes = 2 * kTileBytes;
-constexpr uint32_t kLdsBytes = 2 * kStageBytes;          // 128 KiB
+constexpr uint32_t kCodeRun = (kGemmBN + 32) * 4;        // one code run in LDS, padded: 1152 B
+constexpr uint32_t kLdsA = 0;
+constexpr uint32_t kLdsB = 32768;
+constexpr uint32_t kLdsScales = kLdsB + kCodeChunksPerTile * kCodeRun;  // 32768 + 9216
+constexpr uint32_t kStage = 65536;
+constexpr uint32_t kLdsBytes = 2 * kStage;               // 128 KiB
+static_assert(kLdsScales + kScaleTileBytes <= kStage, "stage overflow");
 
-struct Staged {
-  u32x4 a[8];   // activation: 8 chunks of 8 bf16
-  u32x4 b[8];   // LoRA B: 8 chunks of 8 bf16; W4: b[0..1] = 32 code bytes, b[2].x = 4 scale codes
-};
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-__device__ __forceinline__ void load_stage(const GemmParams& p, int64_t m0, int nt, int kt, int tid,
-                                           Staged& st) {
-  const bool lora = kt >= p.k_tiles;
-  // activation (x*pqs or t'): chunk c = tid + 256 i covers row c/8, 8 bf16 at k-chunk c%8
-  const uint16_t* src = lora ? p.lora_t : p.act;
-  const int64_t ld = lora ? p.lora_t_ld : p.act_ld;
-  const int64_t k0 = static_cast<int64_t>(lora ? kt - p.k_tiles : kt) * BK;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + kThreads * i;
-    int64_t row = m0 + (c >> 3);
-    row = row < p.S ? row : p.S - 1;
-    st.a[i] = *reinterpret_cast<const u32x4*>(src + row * ld + k0 + (c & 7) * 8);
-  }
-  if (lora) {
-    const uint16_t* bt = p.lora_b + (static_cast<int64_t>(nt) * p.r_tiles + (kt - p.k_tiles)) * (BN * BK);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kThreads * i;
-      st.b[i] = *reinterpret_cast<const u32x4*>(bt + (c >> 3) * BK + (c & 7) * 8);
-    }
-  } else {
-    const int64_t tile = static_cast<int64_t>(nt) * p.k_tiles + kt;
-    const uint8_t* cp = p.wcodes + (tile * BN + tid) * kCodeBytesPerRowTile;
-    st.b[0] = *reinterpret_cast<const u32x4*>(cp);
-    st.b[1] = *reinterpret_cast<const u32x4*>(cp + 16);
-    st.b[2].x = *reinterpret_cast<const uint32_t*>(p.wscales + (tile * BN + tid) * kScaleBytesPerRowTile);
-  }
+__device__ __forceinline__ constexpr uint32_t stage_offset_code_run(uint32_t kc) { return kLdsB + kc * kCodeRun; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
-__device__ __forceinline__ void store_stage(uint8_t* stage, bool lora, int tid, const Staged& st) {
-  uint8_t* As = stage;
-  uint8_t* Bs = stage + kTileBytes;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + kThreads * i;
-    *reinterpret_cast<u32x4*>(As + lds_chunk_offset(c >> 3, c & 7)) = st.a[i];
-  }
-  if (lora) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(Bs + lds_chunk_offset(c >> 3, c & 7)) = st.b[i];
-    }
-  } else {
-    // one weight row per thread: 4 scale blocks of 16 elements = 8 chunks of 8 elements
-    const uint32_t sc = st.b[2].x;
-    const uint32_t words[8] = {st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w,
-                               st.b[1].x, st.b[1].y, st.b[1].z, st.b[1].w};
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      const float s = e4m3_to_f32((sc >> (8 * (ch >> 1))) & 0xffu);
-      *reinterpret_cast<u32x4*>(Bs + lds_chunk_offset(tid, ch)) = nvfp4_word_to_bf16x8(words[ch], s);
-    }
-  }
+// 16 bytes per lane from buffer offset voff + soff to LDS at lds + 16 * lane.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(lds), 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+struct Ctx {
+  __amdgpu_buffer_rsrc_t act, lt, codes, scales, lb;
+  // Copy i (of 8 per wave per operand) covers tile rows (8w + i)*8 .. +8; its per-lane offset is
+  // vbase[i & 1] (rows of copy 0 or 1) plus a uniform (i & ~1) * 8 rows, so only two offsets per
+  // operand live in registers.
+  uint32_t vact[2], vlt[2], vtile[2];
+  uint32_t act_rows8, lt_rows8;  // bytes of 8 rows of the activation / t'
+  int k_tiles, r_tiles, wave, lane;
+};
+
+// Issues the copies of K-tile kt (base tiles first, then LoRA tiles) into an LDS stage.
+__device__ __forceinline__ void issue_stage(const Ctx& c, int kt, uint8_t* stage) {
+  const int w = c.wave;
+  if (kt < c.k_tiles) {
+    const uint32_t k_bytes = static_cast<uint32_t>(kt) * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      copy16(c.act, stage + kLdsA + (w * 8 + i) * 1024, c.vact[i & 1], k_bytes + (i & ~1) * c.act_rows8);
+    const uint32_t ct = static_cast<uint32_t>(kt) * kCodeTileBytes;
+    copy16(c.codes, stage + kLdsB + w * kCodeRun, c.lane * 16, ct + w * 1024);
+    copy16(c.codes, stage + kLdsB + (w + 4) * kCodeRun, c.lane * 16, ct + (w + 4) * 1024);
+    if (w == 3) copy16(c.scales, stage + kLdsScales, c.lane * 16, static_cast<uint32_t>(kt) * kScaleTileBytes);
+  } else {
+    const uint32_t rt = static_cast<uint32_t>(kt - c.k_tiles);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      copy16(c.lt, stage + kLdsA + (w * 8 + i) * 1024, c.vlt[i & 1], rt * BK * 2 + (i & ~1) * c.lt_rows8);
+      copy16(c.lb, stage + kLdsB + (w * 8 + i) * 1024, c.vtile[i & 1], rt * kLoraTileBytes + (i & ~1) * 1024);
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_read_a(const uint8_t* stage, uint32_t row, uint32_t chunk) {
+  return *reinterpret_cast<const bf16x8*>(stage + kLdsA + lds_chunk_offset(row, chunk));
+}
+
+// A operand of K-step KK (16 k) for the 8 row tiles: row i*32 + lane%32, k-chunk 2KK + lane/32.
+template <int KK>
+__device__ __forceinline__ void load_a(const uint8_t* stage, uint32_t lane, bf16x8 (&a)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = lds_read_a(stage, i * 32 + (lane & 31), KK * 2 + (lane >> 5));
+}
+
+// 4-bit B operand of K-step KK: one code dword (8 consecutive k) per lane and column tile.
+template <int KK>
+__device__ __forceinline__ void load_codes(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
+                                           uint32_t (&cw)[2]) {
+  const uint32_t run = stage_offset_code_run(KK * 2 + (lane >> 5));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) cw[j] = *reinterpret_cast<const uint32_t*>(stage + run + ncol[j] * 4);
+}
+
+// bf16 B operand of a LoRA K-step KK.
+template <int KK>
+__device__ __forceinline__ void load_b_bf16(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
+                                            bf16x8 (&b)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    b[j] = *reinterpret_cast<const bf16x8*>(stage + kLdsB + lds_chunk_offset(ncol[j], KK * 2 + (lane >> 5)));
+}
+
+// Decode: 8 E2M1 codes times the block scale (byte KK of the row's scale dword) -> bf16 operand.
+template <int KK>
+__device__ __forceinline__ void decode_b(const uint32_t (&cw)[2], const uint32_t (&sdw)[2], bf16x8 (&b)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    b[j] = __builtin_bit_cast(bf16x8, nvfp4_dword_to_bf16x8(cw[j], e4m3_byte_to_f32<KK>(sdw[j])));
+}
+
+__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[8], const bf16x8 (&b)[2], f32x16 (&acc)[8][2]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[0], acc[i][0], 0, 0, 0);
+    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[1], acc[i][1], 0, 0, 0);
+  }
+}
+
+// One 64-deep base K-tile: the A operand and codes of step KK+1 are read from LDS while step KK's
+// 16 MFMAs run (two register sets, a0/a1), and each step's B operand is decoded just before use.
+__device__ __forceinline__ void w4_tile(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
+                                        f32x16 (&acc)[8][2]) {
+  const uint32_t sdw[2] = {*reinterpret_cast<const uint32_t*>(stage + kLdsScales + ncol[0] * 4),
+                           *reinterpret_cast<const uint32_t*>(stage + kLdsScales + ncol[1] * 4)};
+  bf16x8 a0[8], a1[8], b[2];
+  uint32_t c0[2], c1[2];
+  load_a<0>(stage, lane, a0);
+  load_codes<0>(stage, lane, ncol, c0);
+  load_a<1>(stage, lane, a1);
+  load_codes<1>(stage, lane, ncol, c1);
+  decode_b<0>(c0, sdw, b);
+  mfma_block(a0, b, acc);
+  load_a<2>(stage, lane, a0);
+  load_codes<2>(stage, lane, ncol, c0);
+  decode_b<1>(c1, sdw, b);
+  mfma_block(a1, b, acc);
+  load_a<3>(stage, lane, a1);
+  load_codes<3>(stage, lane, ncol, c1);
+  decode_b<2>(c0, sdw, b);
+  mfma_block(a0, b, acc);
+  decode_b<3>(c1, sdw, b);
+  mfma_block(a1, b, acc);
+}
+
+__device__ __forceinline__ void lora_tile(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
+                                          f32x16 (&acc)[8][2]) {
+  bf16x8 a0[8], a1[8], b0[2], b1[2];
+  load_a<0>(stage, lane, a0);
+  load_b_bf16<0>(stage, lane, ncol, b0);
+  load_a<1>(stage, lane, a1);
+  load_b_bf16<1>(stage, lane, ncol, b1);
+  mfma_block(a0, b0, acc);
+  load_a<2>(stage, lane, a0);
+  load_b_bf16<2>(stage, lane, ncol, b0);
+  mfma_block(a1, b1, acc);
+  load_a<3>(stage, lane, a1);
+  load_b_bf16<3>(stage, lane, ncol, b1);
+  mfma_block(a0, b0, acc);
+  mfma_block(a1, b1, acc);
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: keep it scalar
 
   // XCD-aware work index (gridDim.x is a multiple of 8)
   const int per_xcd = gridDim.x >> 3;
   const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (w >= p.m_tiles * p.n_tiles) return;
-  const int mt = w / p.n_tiles, nt = w - mt * p.n_tiles;
+  const int mt = __builtin_amdgcn_readfirstlane(w / p.n_tiles);
+  const int nt = __builtin_amdgcn_readfirstlane(w - mt * p.n_tiles);
   const int64_t m0 = static_cast<int64_t>(mt) * BM;
+
+  Ctx c;
+  c.k_tiles = p.k_tiles;
+  c.r_tiles = p.r_tiles;
+  c.wave = wave;
+  c.lane = lane;
+  c.act = rsrc(p.act, static_cast<uint32_t>(p.S * p.act_ld * 2));
+  c.codes = rsrc(p.wcodes + static_cast<int64_t>(nt) * p.k_tiles * kCodeTileBytes,
+                 static_cast<uint32_t>(p.k_tiles) * kCodeTileBytes);
+  c.scales = rsrc(p.wscales + static_cast<int64_t>(nt) * p.k_tiles * kScaleTileBytes,
+                  static_cast<uint32_t>(p.k_tiles) * kScaleTileBytes);
+  c.lt = rsrc(p.lora_t, p.r_tiles ? static_cast<uint32_t>(p.S * p.lora_t_ld * 2) : 0u);
+  c.lb = rsrc(reinterpret_cast<const uint8_t*>(p.lora_b) + static_cast<int64_t>(nt) * p.r_tiles * kLoraTileBytes,
+              static_cast<uint32_t>(p.r_tiles) * kLoraTileBytes);
+  // lane -> (row, chunk) of each 1 KiB copy this wave issues, matching the swizzled LDS layout:
+  // slot (8w + i)*64 + lane holds row (8w + i)*8 + lane/8 and chunk (lane%8) ^ ((row/2)%8), which
+  // depends on i only through i & 1. Rows at or past S fall outside the buffer and read as zero.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t row = (wave * 8 + h) * 8 + (lane >> 3);
+    const uint32_t chunk = (lane & 7) ^ ((row >> 1) & 7);
+    const uint32_t grow = static_cast<uint32_t>(m0) + row;
+    c.vact[h] = grow * static_cast<uint32_t>(p.act_ld * 2) + chunk * 16;
+    c.vlt[h] = grow * static_cast<uint32_t>(p.lora_t_ld * 2) + chunk * 16;
+    c.vtile[h] = row * 128 + chunk * 16;
+  }
+  c.act_rows8 = static_cast<uint32_t>(p.act_ld * 16);
+  c.lt_rows8 = static_cast<uint32_t>(p.lora_t_ld * 16);
+
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x16{};
+
+  const uint32_t ncol[2] = {static_cast<uint32_t>(wave * 64) + (lane & 31),
+                            static_cast<uint32_t>(wave * 64 + 32) + (lane & 31)};
   const int total = p.k_tiles + p.r_tiles;
 
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  Staged st;
-  load_stage(p, m0, nt, 0, tid, st);
-  store_stage(smem, 0 >= p.k_tiles, tid, st);
+  issue_stage(c, 0, smem);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  const uint32_t a_row0 = wm * 128 + (lane & 31);
-  const uint32_t b_row0 = wn * 128 + (lane & 31);
-  const uint32_t khalf = lane >> 5;
-
-  for (int kt = 0; kt < total; ++kt) {
-    const bool more = kt + 1 < total;
-    if (more) load_stage(p, m0, nt, kt + 1, tid, st);
-
-    const uint8_t* As = smem + (kt & 1) * kStageBytes;
-    const uint8_t* Bs = As + kTileBytes;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(As + lds_chunk_offset(a_row0 + i * 32, kk * 2 + khalf));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_chunk_offset(b_row0 + j * 32, kk * 2 + khalf));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-
-    if (more) store_stage(smem + ((kt + 1) & 1) * kStageBytes, kt + 1 >= p.k_tiles, tid, st);
+  // base K-tiles (4-bit weight), then the LoRA K-tiles (bf16 B); the copy of tile kt + 1 is in
+  // flight while tile kt is multiplied, and one barrier per tile hands the stages over
+  for (int kt = 0; kt < p.k_tiles; ++kt) {
+    const uint8_t* stage = smem + (kt & 1) * kStage;
+    if (kt + 1 < total) issue_stage(c, kt + 1, smem + ((kt + 1) & 1) * kStage);
+    w4_tile(stage, lane, ncol, acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  for (int kt = p.k_tiles; kt < total; ++kt) {
+    const uint8_t* stage = smem + (kt & 1) * kStage;
+    if (kt + 1 < total) issue_stage(c, kt + 1, smem + ((kt + 1) & 1) * kStage);
+    lora_tile(stage, lane, ncol, acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // Epilogue. Accumulator register r of lane l in a 32x32 tile holds
   // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
   const float scale = p.ts * (p.ts_dev ? *p.ts_dev : 1.0f);
-  const int col_lane = lane & 31;
   const int row_lane = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + row_lane + (r & 3);
+      const int64_t row = m0 + i * 32 + (r >> 2) * 8 + row_lane + (r & 3);
       if (row >= p.S) continue;
       uint16_t* orow = p.out + row * p.out_ld;
       if (EPI == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = wn * 128 + j * 32 + col_lane;
-          const int64_t n = p.gate_up ? packed_row_source(nt, c, true, p.n_out) : static_cast<int64_t>(nt) * BN + c;
+        for (int j = 0; j < 2; ++j) {
+          const int cl = static_cast<int>(ncol[j]);
+          const int64_t n = p.gate_up ? packed_row_source(nt, cl, true, p.n_out) : static_cast<int64_t>(nt) * BN + cl;
           if (n >= 0 && n < p.n_out) orow[n] = static_cast<uint16_t>(f32_to_bf16_rne(scale * acc[i][j][r]));
         }
       } else {
-        // tile columns alternate in 32-wide groups: gate j0..j0+31, then up j0..j0+31
-#pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const int64_t n = static_cast<int64_t>(nt) * (BN / 2) + (wn * 2 + j / 2) * 32 + col_lane;
-          if (n < p.n_out) {
-            const float g = scale * acc[i][j][r];
-            const float u = scale * acc[i][j + 1][r];
-            orow[n] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * u));
-          }
+        // this wave's 64 tile columns are 32 gate columns then the 32 matching up columns
+        const int64_t n = static_cast<int64_t>(nt) * (BN / 2) + wave * 32 + (lane & 31);
+        if (n < p.n_out) {
+          const float g = scale * acc[i][0][r];
+          const float u = scale * acc[i][1][r];
+          orow[n] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * u));
         }
       }
     }
@@ -200,10 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
 
 size_t gemm_w4_lds_bytes() { return kLdsBytes; }
 
-hipError_t launch_gemm_w4(const GemmParams& p, Epilogue epi, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
-  const int64_t grid = (items + 7) / 8 * 8;
-  if (grid == 0) return hipSuccess;
+hipError_t launch_gemm_w4(const GemmParams& p0, Epilogue epi, hipStream_t stream) {
   const void* fn = epi == Epilogue::Plain ? reinterpret_cast<const void*>(&gemm_w4_kernel<0>)
                                           : reinterpret_cast<const void*>(&gemm_w4_kernel<1>);
   static std::once_flag once[2];
@@ -213,11 +299,27 @@ hipError_t launch_gemm_w4(const GemmParams& p, Epilogue epi, hipStream_t stream)
     attr_err[e] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   });
   if (attr_err[e] != hipSuccess) return attr_err[e];
-  if (epi == Epilogue::Plain)
-    hipLaunchKernelGGL(gemm_w4_kernel<0>, dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
-  else
-    hipLaunchKernelGGL(gemm_w4_kernel<1>, dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
-  return hipGetLastError();
+
+  // Buffer offsets are 32-bit: launch row ranges whose activation and t' spans stay below 2 GiB.
+  const int64_t row_bytes = std::max<int64_t>(p0.act_ld, p0.lora_t_ld) * 2;
+  const int64_t rows_per_launch = ((int64_t{1} << 31) - 1) / row_bytes / BM * BM;
+  for (int64_t r0 = 0; r0 < p0.S; r0 += rows_per_launch) {
+    GemmParams p = p0;
+    p.S = std::min<int64_t>(rows_per_launch, p0.S - r0);
+    p.act = p0.act + r0 * p0.act_ld;
+    p.lora_t = p0.lora_t ? p0.lora_t + r0 * p0.lora_t_ld : nullptr;
+    p.out = p0.out + r0 * p0.out_ld;
+    p.m_tiles = static_cast<int32_t>((p.S + BM - 1) / BM);
+    const int64_t items = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
+    const int64_t grid = (items + 7) / 8 * 8;
+    if (epi == Epilogue::Plain)
+      hipLaunchKernelGGL(gemm_w4_kernel<0>, dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
+    else
+      hipLaunchKernelGGL(gemm_w4_kernel<1>, dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace h3q

@@ -279,27 +279,31 @@ h3q_status h3q_pack_weight(void* stream, const uint8_t* codes, const uint8_t* sc
   w->k_tiles = static_cast<int32_t>(w->K_pad / kGemmBK);
   w->n_tiles = static_cast<int32_t>(gu ? (N / 2 + kGemmBN / 2 - 1) / (kGemmBN / 2) : (N + kGemmBN - 1) / kGemmBN);
 
-  // tile on the host: byte moves only
-  const int64_t prow = static_cast<int64_t>(w->n_tiles) * kGemmBN;
-  std::vector<uint8_t> tc(static_cast<size_t>(prow * w->k_tiles * kCodeBytesPerRowTile), 0);
-  std::vector<uint8_t> tsc(static_cast<size_t>(prow * w->k_tiles * kScaleBytesPerRowTile), 0);
+  // tile on the host: byte moves only (layout in h3q_kernels.hpp)
+  const int64_t tiles = static_cast<int64_t>(w->n_tiles) * w->k_tiles;
+  std::vector<uint32_t> tc(static_cast<size_t>(tiles * kCodeChunksPerTile * kGemmBN), 0u);
+  std::vector<uint32_t> tsc(static_cast<size_t>(tiles * kGemmBN), 0u);
   for (int64_t nt = 0; nt < w->n_tiles; ++nt)
     for (int64_t c = 0; c < kGemmBN; ++c) {
       const int64_t n = packed_row_source(nt, c, gu, N);
       if (n < 0) continue;
+      const uint8_t* crow = codes + n * (K / 2);
+      const uint8_t* srow = scales + n * (K / 16);
       for (int64_t kt = 0; kt < w->k_tiles; ++kt) {
-        const int64_t tile_row = (nt * w->k_tiles + kt) * kGemmBN + c;
-        const int64_t cb = std::min<int64_t>(kCodeBytesPerRowTile, K / 2 - kt * kCodeBytesPerRowTile);
-        const int64_t sb = std::min<int64_t>(kScaleBytesPerRowTile, K / 16 - kt * kScaleBytesPerRowTile);
-        std::memcpy(&tc[tile_row * kCodeBytesPerRowTile], codes + n * (K / 2) + kt * kCodeBytesPerRowTile, cb);
-        std::memcpy(&tsc[tile_row * kScaleBytesPerRowTile], scales + n * (K / 16) + kt * kScaleBytesPerRowTile, sb);
+        const int64_t tile = nt * w->k_tiles + kt;
+        for (int64_t kc = 0; kc < kCodeChunksPerTile && kt * kGemmBK + kc * 8 < K; ++kc)
+          std::memcpy(&tc[(tile * kCodeChunksPerTile + kc) * kGemmBN + c], crow + (kt * kGemmBK + kc * 8) / 2, 4);
+        uint32_t sw = 0;
+        for (int64_t b = 0; b < kGemmBK / 16 && kt * (kGemmBK / 16) + b < K / 16; ++b)
+          sw |= static_cast<uint32_t>(srow[kt * (kGemmBK / 16) + b]) << (8 * b);
+        tsc[tile * kGemmBN + c] = sw;
       }
     }
-  w->codes_bytes = tc.size();
-  w->scales_bytes = tsc.size();
+  w->codes_bytes = tc.size() * 4;
+  w->scales_bytes = tsc.size() * 4;
   (void)stream;  // synchronous copies: the caller's buffers are host memory
-  h3q_status st = copy_to_device(reinterpret_cast<void**>(&w->codes), tc.data(), tc.size());
-  if (st == H3Q_OK) st = copy_to_device(reinterpret_cast<void**>(&w->scales), tsc.data(), tsc.size());
+  h3q_status st = copy_to_device(reinterpret_cast<void**>(&w->codes), tc.data(), w->codes_bytes);
+  if (st == H3Q_OK) st = copy_to_device(reinterpret_cast<void**>(&w->scales), tsc.data(), w->scales_bytes);
   if (st != H3Q_OK) {
     if (w->codes) (void)hipFree(w->codes);
     delete w;
@@ -521,7 +525,8 @@ h3q_status h3q_quantize_nvfp4(void* stream_, const uint16_t* x, int64_t S, int64
 h3q_status h3q_debug_dequant(void* stream, h3q_weight w, uint16_t* wq) {
   if (!live(w)) return fail(H3Q_E_ARG, "debug_dequant: not a live weight handle");
   if (!wq || !aligned16(wq)) return fail(H3Q_E_ARG, "debug_dequant: output must be non-null and 16-byte aligned");
-  DequantParams p{w->codes, w->scales, w->n_tiles, w->k_tiles, gate_up(w), w->N, w->K, wq};
+  DequantParams p{reinterpret_cast<const uint32_t*>(w->codes), reinterpret_cast<const uint32_t*>(w->scales),
+                  w->n_tiles, w->k_tiles, gate_up(w), w->N, w->K, wq};
   hipError_t e = launch_debug_dequant(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(H3Q_E_HIP, "debug_dequant launch: %s", hipGetErrorString(e));
   return ok();

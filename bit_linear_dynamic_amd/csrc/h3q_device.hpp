@@ -31,36 +31,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// E4M3 ("FN", bias 7) scale code -> fp32, for the non-negative finite codes 0x00..0x7E that
-// packing and quantization produce. Exponent 0 is subnormal: m * 2^-9.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : static_cast<float>(m) * 0x1p-9f;
+// E4M3 ("FN": bias 7, no inf, NaN = 0x7F) scale in byte SEL of w -> fp32. gfx950's
+// v_cvt_f32_fp8 decodes the OCP E4M3FN variant (checked over all 256 codes against the format table).
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), SEL);
 }
 
-// Magnitude of an E2M1 code (its low 3 bits) as fp32 bits: exponent field e (bias 1), mantissa m.
-__device__ __forceinline__ uint32_t e2m1_mag_f32_bits(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  return e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3f000000u : 0u);
+// Two bf16 (low half = a) from two fp32 whose low 16 bits are zero (exact bf16 values).
+__device__ __forceinline__ uint32_t pack_exact_bf16x2(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
-// One element: bf16 bits of E2M1(c) * s for a non-negative scale s. The fp32 product is exact and
-// its low 16 bits are zero, so taking the high half is the exact bf16; the sign comes from the code
-// (IEEE product sign, so negative zero codes and zero scales give -0).
-__device__ __forceinline__ uint32_t nvfp4_elem_bf16(uint32_t c, float s) {
-  const float v = __uint_as_float(e2m1_mag_f32_bits(c)) * s;
-  return (__float_as_uint(v) >> 16) | ((c & 8u) << 12);
-}
-
-// Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) times scale s ->
-// eight bf16 packed two per word, element order preserved.
-__device__ __forceinline__ u32x4 nvfp4_word_to_bf16x8(uint32_t w, float s) {
+// Eight E2M1 codes (one dword: element i in nibble i, low nibble first) times the block scale s ->
+// eight bf16 in element order, two per dword. v_cvt_scalef32_pk_f32_fp4 with scale 1.0 yields the
+// exact E2M1 values (its scale operand contributes only a power of two, so the E4M3 mantissa must
+// be applied separately); the fp32 product with s is exact and its high half is the exact bf16.
+__device__ __forceinline__ u32x4 nvfp4_dword_to_bf16x8(uint32_t cw, float s) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
   u32x4 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t byte = (w >> (8 * i)) & 0xffu;
-    out[i] = nvfp4_elem_bf16(byte & 0xfu, s) | (nvfp4_elem_bf16(byte >> 4, s) << 16);
-  }
+  out.x = pack_exact_bf16x2(v0.x * s, v0.y * s);
+  out.y = pack_exact_bf16x2(v1.x * s, v1.y * s);
+  out.z = pack_exact_bf16x2(v2.x * s, v2.y * s);
+  out.w = pack_exact_bf16x2(v3.x * s, v3.y * s);
   return out;
 }
 

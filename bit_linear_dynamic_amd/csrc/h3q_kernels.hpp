@@ -12,16 +12,21 @@ namespace h3q {
 constexpr int kGemmBM = 256;   // rows of x per workgroup tile
 constexpr int kGemmBN = 256;   // output columns (packed weight rows) per workgroup tile
 constexpr int kGemmBK = 64;    // K per pipeline stage
-constexpr int kCodeBytesPerRowTile = kGemmBK / 2;   // 32 bytes of E2M1 codes per row per K-tile
-constexpr int kScaleBytesPerRowTile = kGemmBK / 16; // 4 E4M3 scales per row per K-tile
+// Packed codes: for column tile nt and K-tile kt, chunk kc (8 consecutive k) of all 256 rows is one
+// run of 256 dwords: dword [((nt*k_tiles + kt)*8 + kc)*256 + c] holds row c's 8 codes, element i in
+// nibble i. Packed scales: dword [(nt*k_tiles + kt)*256 + c] holds row c's 4 E4M3 block scales.
+constexpr int kCodeChunksPerTile = kGemmBK / 8;          // 8
+constexpr int kCodeTileBytes = kCodeChunksPerTile * kGemmBN * 4;  // 8 KiB per (nt, kt)
+constexpr int kScaleTileBytes = kGemmBN * 4;              // 1 KiB per (nt, kt)
+constexpr int kLoraTileBytes = kGemmBN * kGemmBK * 2;     // 32 KiB per (nt, rank tile)
 
 struct GemmParams {
   const uint16_t* act;      // bf16 [S][act_ld]: activation operand (x, x*pqs, or decoded NVFP4 x)
   int64_t act_ld;
   const uint16_t* lora_t;   // bf16 [S][r_pad]: f * (A x), folded in as extra K-columns; or null
   int64_t lora_t_ld;
-  const uint8_t* wcodes;    // [n_tiles][k_tiles][256][32]
-  const uint8_t* wscales;   // [n_tiles][k_tiles][256][4]
+  const uint8_t* wcodes;    // packed codes (layout above)
+  const uint8_t* wscales;   // packed scales (layout above)
   const uint16_t* lora_b;   // bf16 [n_tiles][r_tiles][256][64], rows in the weight's tile order
   int64_t S;
   int32_t k_tiles;          // K_pad / 64
@@ -91,8 +96,8 @@ __host__ __device__ inline int64_t packed_row_source(int64_t nt, int64_t c, bool
 }
 
 struct DequantParams {
-  const uint8_t* wcodes;
-  const uint8_t* wscales;
+  const uint32_t* wcodes_dw;
+  const uint32_t* wscales_dw;
   int32_t n_tiles, k_tiles;
   bool gate_up;
   int64_t N, K;

@@ -1,5 +1,5 @@
 // misc.hip -- diagnostic kernel: the packed weight decoded back to the caller's [N][K] order with
-// the same decode routine the GEMM uses (E2M1 * E4M3, exact in bf16, without the tensor scale).
+// the decode routine the GEMM uses (E2M1 * E4M3, exact in bf16, without the tensor scale).
 #include "h3q_device.hpp"
 #include "h3q_kernels.hpp"
 
@@ -7,7 +7,20 @@ namespace h3q {
 
 namespace {
 
-// one thread per (packed row, K-tile): 32 code bytes + 4 scales -> 64 bf16
+template <int SEL>
+__device__ __forceinline__ void decode_block(const DequantParams& p, int64_t tile, int64_t c, uint32_t sc,
+                                             uint16_t* dst, int64_t k0) {
+  const float s = e4m3_byte_to_f32<SEL>(sc);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kc = 2 * SEL + h;
+    if (k0 + kc * 8 >= p.K) return;
+    const uint32_t cw = p.wcodes_dw[(tile * kCodeChunksPerTile + kc) * kGemmBN + c];
+    *reinterpret_cast<u32x4*>(dst + kc * 8) = nvfp4_dword_to_bf16x8(cw, s);
+  }
+}
+
+// one thread per (packed row, K-tile): 8 code dwords + 1 scale dword -> 64 bf16
 __global__ __launch_bounds__(256) void debug_dequant_kernel(DequantParams p) {
   const int64_t rows = static_cast<int64_t>(p.n_tiles) * kGemmBN;
   const int64_t total = rows * p.k_tiles;
@@ -19,15 +32,13 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(DequantParams p) {
     const int64_t n = packed_row_source(nt, c, p.gate_up, p.N);
     if (n < 0) continue;
     const int64_t tile = nt * p.k_tiles + kt;
-    const uint8_t* cp = p.wcodes + (tile * kGemmBN + c) * kCodeBytesPerRowTile;
-    const uint32_t sc = *reinterpret_cast<const uint32_t*>(p.wscales + (tile * kGemmBN + c) * kScaleBytesPerRowTile);
-    for (int ch = 0; ch < 8; ++ch) {
-      const int64_t k = kt * kGemmBK + ch * 8;
-      if (k >= p.K) break;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(cp + ch * 4);
-      const u32x4 v = nvfp4_word_to_bf16x8(w, e4m3_to_f32((sc >> (8 * (ch >> 1))) & 0xffu));
-      *reinterpret_cast<u32x4*>(p.out + n * p.K + k) = v;
-    }
+    const uint32_t sc = p.wscales_dw[tile * kGemmBN + c];
+    const int64_t k0 = kt * kGemmBK;
+    uint16_t* dst = p.out + n * p.K + k0;
+    decode_block<0>(p, tile, c, sc, dst, k0);
+    decode_block<1>(p, tile, c, sc, dst, k0);
+    decode_block<2>(p, tile, c, sc, dst, k0);
+    decode_block<3>(p, tile, c, sc, dst, k0);
   }
 }
 

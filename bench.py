@@ -36,10 +36,14 @@ def parse():
     ap.add_argument("--S", type=int, default=37726)
     ap.add_argument("--cpu-rows", type=int, default=24, help="rows per projection in the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--proj", choices=["qkv", "attn_out", "gate_up", "down"], default=None,
+                    help="profiling aid: time one projection only (the JSON line then covers only it)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="profiling aid: run only a plain device copy of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
 
 
-def build_block(S, device):
+def build_block(S, device, only=None):
     """Pack the four projections (weights quantized on the device by h3q_quantize_nvfp4 from
     N(0, 0.02) draws) and register one adapter each; returns per-projection state."""
     import torch
@@ -51,6 +55,8 @@ def build_block(S, device):
     projs = []
     xs = {}
     for i, p in enumerate(wl.BLOCK):
+        if only is not None and p.name != only:
+            continue
         w = synth.weight_fp32(p.N, p.K, synth.seed_of(3, i, synth.W), device).to(torch.bfloat16)
         codes, scales, ts = h3q.h3q_quantize_nvfp4(w)
         torch.cuda.synchronize()
@@ -120,9 +126,18 @@ def main():
     from bit_linear_dynamic_amd import workloads as wl
 
     device = "cuda"
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=device)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_mib": args.calibrate_copy, "launches": 3}), flush=True)
+        return
     S = args.S
-    print(f"bench: building the four projections at S={S}", file=sys.stderr, flush=True)
-    projs = build_block(S, device)
+    print(f"bench: building the projections at S={S}", file=sys.stderr, flush=True)
+    projs = build_block(S, device, args.proj)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -171,6 +186,7 @@ def main():
 
     line = {
         "metric": "effective TFLOP/s (+% bf16 MFMA peak) of W4+LoRA linear, S=37726",
+        "only_projection": args.proj,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

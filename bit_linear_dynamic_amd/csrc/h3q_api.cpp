@@ -196,7 +196,7 @@ struct Adapter {
   int32_t rank = 0, r_pad = 0;
   float alpha = 0.0f;
   uint16_t* A = nullptr;  // [r_pad][K_pad]
-  uint16_t* B = nullptr;  // [n_tiles][r_pad/64][256][64]
+  uint16_t* B = nullptr;  // [n_tiles][r_pad/32][256][32]
 };
 
 struct h3q_weight_s {
@@ -357,14 +357,14 @@ h3q_status h3q_register_adapter(h3q_weight w, int32_t id, const uint16_t* A, con
   const int64_t K = w->K, Kp = w->K_pad, N = w->N;
   std::vector<uint16_t> Ah(static_cast<size_t>(a.r_pad * Kp), 0);
   for (int64_t j = 0; j < rank; ++j) std::memcpy(&Ah[j * Kp], A + j * K, K * sizeof(uint16_t));
-  const int64_t r_tiles = a.r_pad / 64;
-  std::vector<uint16_t> Bh(static_cast<size_t>(int64_t{w->n_tiles} * r_tiles * kGemmBN * 64), 0);
+  const int64_t r_tiles = a.r_pad / kLoraBK;
+  std::vector<uint16_t> Bh(static_cast<size_t>(int64_t{w->n_tiles} * r_tiles * kGemmBN * kLoraBK), 0);
   for (int64_t nt = 0; nt < w->n_tiles; ++nt)
     for (int64_t c = 0; c < kGemmBN; ++c) {
       const int64_t n = packed_row_source(nt, c, gate_up(w), N);
       if (n < 0) continue;
       for (int64_t j = 0; j < rank; ++j)
-        Bh[((nt * r_tiles + j / 64) * kGemmBN + c) * 64 + j % 64] = B[n * rank + j];
+        Bh[((nt * r_tiles + j / kLoraBK) * kGemmBN + c) * kLoraBK + j % kLoraBK] = B[n * rank + j];
     }
   h3q_status st = copy_to_device(reinterpret_cast<void**>(&a.A), Ah.data(), Ah.size() * 2);
   if (st == H3Q_OK) st = copy_to_device(reinterpret_cast<void**>(&a.B), Bh.data(), Bh.size() * 2);
@@ -479,7 +479,7 @@ h3q_status h3q_linear_ex(void* stream_, const uint16_t* x, int64_t S, const floa
   g.lora_b = lora ? ad->B : nullptr;
   g.S = S;
   g.k_tiles = w->k_tiles;
-  g.r_tiles = lora ? ad->r_pad / 64 : 0;
+  g.r_tiles = lora ? ad->r_pad / kLoraBK : 0;
   g.m_tiles = static_cast<int32_t>((S + kGemmBM - 1) / kGemmBM);
   g.n_tiles = w->n_tiles;
   g.n_out = n_out;

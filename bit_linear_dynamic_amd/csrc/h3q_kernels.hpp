@@ -18,7 +18,9 @@ constexpr int kGemmBK = 64;    // K per pipeline stage
 constexpr int kCodeChunksPerTile = kGemmBK / 8;          // 8
 constexpr int kCodeTileBytes = kCodeChunksPerTile * kGemmBN * 4;  // 8 KiB per (nt, kt)
 constexpr int kScaleTileBytes = kGemmBN * 4;              // 1 KiB per (nt, kt)
-constexpr int kLoraTileBytes = kGemmBN * kGemmBK * 2;     // 32 KiB per (nt, rank tile)
+// LoRA K-tiles are 32 deep (bf16 B and t' tiles of 16 KiB each fit the base tile's LDS stage).
+constexpr int kLoraBK = 32;
+constexpr int kLoraTileBytes = kGemmBN * kLoraBK * 2;     // 16 KiB per (nt, rank tile)
 
 struct GemmParams {
   const uint16_t* act;      // bf16 [S][act_ld]: activation operand (x, x*pqs, or decoded NVFP4 x)
@@ -27,10 +29,10 @@ struct GemmParams {
   int64_t lora_t_ld;
   const uint8_t* wcodes;    // packed codes (layout above)
   const uint8_t* wscales;   // packed scales (layout above)
-  const uint16_t* lora_b;   // bf16 [n_tiles][r_tiles][256][64], rows in the weight's tile order
+  const uint16_t* lora_b;   // bf16 [n_tiles][r_tiles][256][32], rows in the weight's tile order
   int64_t S;
   int32_t k_tiles;          // K_pad / 64
-  int32_t r_tiles;          // r_pad / 64 (0: no adapter)
+  int32_t r_tiles;          // r_pad / 32 (0: no adapter)
   int32_t m_tiles, n_tiles;
   int64_t n_out;            // valid output columns (N, or N/2 for SwiGLU)
   int32_t gate_up;          // weight packed with interleaved gate/up column tiles

@@ -127,94 +127,87 @@ __device__ __forceinline__ void issue_tile(const Ctx& c, int kt, uint8_t* stage)
   }
 }
 
-// A operand of K-step KK (16 k) for the 8 row tiles: row i*32 + lane%32, chunk 2KK + lane/32.
-template <int KK>
-__device__ __forceinline__ void load_a64(const uint8_t* stage, uint32_t lane, bf16x8 (&a)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    a[i] = *reinterpret_cast<const bf16x8*>(stage + kLdsA + slot64(i * 32 + (lane & 31), KK * 2 + (lane >> 5)));
+// ------------------------------------------------------------------------------------------------
+// K-steps. One asm block per 16-deep K-step (instruction order in gemm_w4_steps.inc); the blocks
+// chain through their register operands: a step's "next" outputs are the following step's inputs.
+// ------------------------------------------------------------------------------------------------
+#include "gemm_w4_steps.inc"
+
+#define H3Q_ACC(acc)                                                                            \
+  [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]),   \
+  [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]),   \
+  [c40] "+a"(acc[4][0]), [c41] "+a"(acc[4][1]), [c50] "+a"(acc[5][0]), [c51] "+a"(acc[5][1]),   \
+  [c60] "+a"(acc[6][0]), [c61] "+a"(acc[6][1]), [c70] "+a"(acc[7][0]), [c71] "+a"(acc[7][1])
+#define H3Q_A_IN(a)                                                                             \
+  [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [a4] "v"(a[4]), [a5] "v"(a[5]), \
+  [a6] "v"(a[6]), [a7] "v"(a[7])
+#define H3Q_A_OUT(n)                                                                            \
+  [n0] "=&v"(n[0]), [n1] "=&v"(n[1]), [n2] "=&v"(n[2]), [n3] "=&v"(n[3]), [n4] "=&v"(n[4]),    \
+  [n5] "=&v"(n[5]), [n6] "=&v"(n[6]), [n7] "=&v"(n[7])
+#define H3Q_B_IN(b)                                                                             \
+  [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]), [b4] "v"(b[4]), [b5] "v"(b[5]), \
+  [b6] "v"(b[6]), [b7] "v"(b[7])
+#define H3Q_B_OUT(m)                                                                            \
+  [m0] "=&v"(m[0]), [m1] "=&v"(m[1]), [m2] "=&v"(m[2]), [m3] "=&v"(m[3]), [m4] "=&v"(m[4]),    \
+  [m5] "=&v"(m[5]), [m6] "=&v"(m[6]), [m7] "=&v"(m[7])
+#define H3Q_STEP_CLOBBERS                                                                       \
+  "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", \
+  "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory"
+
+typedef uint32_t bw_t[8];  // a decoded W4 B operand: 2 column tiles x 4 dwords of bf16 pairs
+
+constexpr uint32_t kPermHighHalves = 0x07060302u;  // v_perm_b32: high 16 bits of each source
+
+// base step, next = K-step of the same base tile (scales s0/s1 of that step given)
+__device__ __forceinline__ void step_bb(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
+                                        bw_t& m, float s0, float s1, uint32_t aaddr, uint32_t caddr) {
+  asm volatile(H3Q_STEP_BB_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m)
+               : H3Q_A_IN(a), H3Q_B_IN(b), [s0] "v"(s0), [s1] "v"(s1), [aaddr] "v"(aaddr), [caddr] "v"(caddr),
+                 [sel] "s"(kPermHighHalves)
+               : H3Q_STEP_CLOBBERS);
 }
-template <int KK>
-__device__ __forceinline__ void load_a32(const uint8_t* stage, uint32_t lane, bf16x8 (&a)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    a[i] = *reinterpret_cast<const bf16x8*>(stage + kLdsA + slot32(i * 32 + (lane & 31), KK * 2 + (lane >> 5)));
+// base step, next = first K-step of a new base tile (its scale dwords d0/d1 are read here too)
+__device__ __forceinline__ void step_bbn(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
+                                         bw_t& m, uint32_t (&d)[2], uint32_t aaddr, uint32_t caddr, uint32_t saddr) {
+  asm volatile(H3Q_STEP_BBN_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [d0] "=&v"(d[0]), [d1] "=&v"(d[1])
+               : H3Q_A_IN(a), H3Q_B_IN(b), [aaddr] "v"(aaddr), [caddr] "v"(caddr), [saddr] "v"(saddr),
+                 [sel] "s"(kPermHighHalves)
+               : H3Q_STEP_CLOBBERS);
+}
+// base step, next = a LoRA K-step
+__device__ __forceinline__ void step_bl(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
+                                        bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr) {
+  asm volatile(H3Q_STEP_BL_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1])
+               : H3Q_A_IN(a), H3Q_B_IN(b), [aaddr] "v"(aaddr), [baddr] "v"(baddr)
+               : H3Q_STEP_CLOBBERS);
+}
+// base step, last of the tile loop
+__device__ __forceinline__ void step_bn(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b) {
+  asm volatile(H3Q_STEP_BN_ASM : H3Q_ACC(acc) : H3Q_A_IN(a), H3Q_B_IN(b) : H3Q_STEP_CLOBBERS);
+}
+// LoRA step, next = a LoRA K-step
+__device__ __forceinline__ void step_ll(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bf16x8 (&l)[2],
+                                        bf16x8 (&n)[8], bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr) {
+  asm volatile(H3Q_STEP_LL_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1])
+               : H3Q_A_IN(a), [l0] "v"(l[0]), [l1] "v"(l[1]), [aaddr] "v"(aaddr), [baddr] "v"(baddr)
+               : H3Q_STEP_CLOBBERS);
+}
+// LoRA step, last of the tile loop
+__device__ __forceinline__ void step_ln(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bf16x8 (&l)[2]) {
+  asm volatile(H3Q_STEP_LN_ASM : H3Q_ACC(acc) : H3Q_A_IN(a), [l0] "v"(l[0]), [l1] "v"(l[1]) : H3Q_STEP_CLOBBERS);
 }
 
-// 4-bit B operand of K-step KK: one code dword (8 consecutive k) per lane and column tile.
-template <int KK>
-__device__ __forceinline__ void load_codes(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
-                                           uint32_t (&cw)[2]) {
-  const uint32_t run = kLdsCodes + (KK * 2 + (lane >> 5)) * kCodeRun;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) cw[j] = *reinterpret_cast<const uint32_t*>(stage + run + ncol[j] * 4);
+// LDS byte address of a pointer into the dynamic shared array.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-// bf16 B operand of LoRA K-step KK.
-template <int KK>
-__device__ __forceinline__ void load_b32(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
-                                         bf16x8 (&b)[2]) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    b[j] = *reinterpret_cast<const bf16x8*>(stage + kLdsLoraB + slot32(ncol[j], KK * 2 + (lane >> 5)));
-}
-
-// Decode: 8 E2M1 codes times the block scale (byte KK of the row's scale dword) -> bf16 operand.
-template <int KK>
-__device__ __forceinline__ void decode_b(const uint32_t (&cw)[2], const uint32_t (&sdw)[2], bf16x8 (&b)[2]) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    b[j] = __builtin_bit_cast(bf16x8, nvfp4_dword_to_bf16x8(cw[j], e4m3_byte_to_f32<KK>(sdw[j])));
-}
-
-__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[8], const bf16x8 (&b)[2], f32x16 (&acc)[8][2]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[0], acc[i][0], 0, 0, 0);
-    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[1], acc[i][1], 0, 0, 0);
-  }
-}
-
-// One 64-deep base K-tile: the A operand and codes of step KK+1 are read from LDS while step KK's
-// 16 MFMAs run (two register sets), and each step's B operand is decoded just before use.
-__device__ __forceinline__ void base_tile(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
-                                          f32x16 (&acc)[8][2]) {
-  const uint32_t sdw[2] = {*reinterpret_cast<const uint32_t*>(stage + kLdsScales + ncol[0] * 4),
-                           *reinterpret_cast<const uint32_t*>(stage + kLdsScales + ncol[1] * 4)};
-  bf16x8 a0[8], a1[8], b[2];
-  uint32_t c0[2], c1[2];
-  load_a64<0>(stage, lane, a0);
-  load_codes<0>(stage, lane, ncol, c0);
-  load_a64<1>(stage, lane, a1);
-  load_codes<1>(stage, lane, ncol, c1);
-  decode_b<0>(c0, sdw, b);
-  mfma_block(a0, b, acc);
-  load_a64<2>(stage, lane, a0);
-  load_codes<2>(stage, lane, ncol, c0);
-  decode_b<1>(c1, sdw, b);
-  mfma_block(a1, b, acc);
-  load_a64<3>(stage, lane, a1);
-  load_codes<3>(stage, lane, ncol, c1);
-  decode_b<2>(c0, sdw, b);
-  mfma_block(a0, b, acc);
-  decode_b<3>(c1, sdw, b);
-  mfma_block(a1, b, acc);
-}
-
-// One 32-deep LoRA K-tile (t' x B in bf16).
-__device__ __forceinline__ void lora_tile(const uint8_t* stage, uint32_t lane, const uint32_t (&ncol)[2],
-                                          f32x16 (&acc)[8][2]) {
-  bf16x8 a0[8], a1[8], b0[2], b1[2];
-  load_a32<0>(stage, lane, a0);
-  load_b32<0>(stage, lane, ncol, b0);
-  load_a32<1>(stage, lane, a1);
-  load_b32<1>(stage, lane, ncol, b1);
-  mfma_block(a0, b0, acc);
-  mfma_block(a1, b1, acc);
-}
-
-// Waits for every copy except the newest tile's (`newest` = the tile just issued, -1 if none),
-// then barriers.
+// Waits for every copy except those of the newest tile in flight (`newest`, -1 if none), then
+// barriers.
 __device__ __forceinline__ void handover(int newest, int k_tiles) {
   if (newest < 0)
     stage_barrier<0>();
@@ -224,7 +217,21 @@ __device__ __forceinline__ void handover(int newest, int k_tiles) {
     stage_barrier<kCopiesLora>();
 }
 
-template <int EPI>
+// Prologue wait: tile 0 landed while tiles 1 and 2 (if any) stay in flight.
+__device__ __forceinline__ void first_handover(int total, int k_tiles) {
+  const int n1 = total > 1 ? (1 < k_tiles ? kCopiesBase : kCopiesLora) : 0;
+  const int n2 = total > 2 ? (2 < k_tiles ? kCopiesBase : kCopiesLora) : 0;
+  switch (n1 + n2) {
+    case 2 * kCopiesBase: stage_barrier<2 * kCopiesBase>(); break;
+    case kCopiesBase + kCopiesLora: stage_barrier<kCopiesBase + kCopiesLora>(); break;
+    case 2 * kCopiesLora: stage_barrier<2 * kCopiesLora>(); break;
+    case kCopiesBase: stage_barrier<kCopiesBase>(); break;
+    case kCopiesLora: stage_barrier<kCopiesLora>(); break;
+    default: stage_barrier<0>(); break;
+  }
+}
+
+template <int EPI, bool LORA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -270,37 +277,120 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   c.act_rows8 = static_cast<uint32_t>(p.act_ld * 16);
   c.lt_rows16 = static_cast<uint32_t>(p.lora_t_ld * 32);
 
+  // accumulators: zeroed in place in AGPRs (an MFMA of zero operands with C = 0), so that they live
+  // in AGPRs from the first to the last K-step
   f32x16 acc[8][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  {
+    const bf16x8 z = {};
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %[c00], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c01], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c10], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c11], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c20], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c21], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c30], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c31], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c40], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c41], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c50], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c51], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c60], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c61], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c70], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c71], %[z], %[z], 0"
+        : [c00] "=a"(acc[0][0]), [c01] "=a"(acc[0][1]), [c10] "=a"(acc[1][0]), [c11] "=a"(acc[1][1]),
+          [c20] "=a"(acc[2][0]), [c21] "=a"(acc[2][1]), [c30] "=a"(acc[3][0]), [c31] "=a"(acc[3][1]),
+          [c40] "=a"(acc[4][0]), [c41] "=a"(acc[4][1]), [c50] "=a"(acc[5][0]), [c51] "=a"(acc[5][1]),
+          [c60] "=a"(acc[6][0]), [c61] "=a"(acc[6][1]), [c70] "=a"(acc[7][0]), [c71] "=a"(acc[7][1])
+        : [z] "v"(z));
+  }
 
   const uint32_t ncol[2] = {static_cast<uint32_t>(wave * 64) + (lane & 31),
                             static_cast<uint32_t>(wave * 64 + 32) + (lane & 31)};
   const int total = p.k_tiles + p.r_tiles;
 
-  // prologue: tiles 0 and 1 in flight; wait for tile 0
+  // Per-lane LDS offsets of the MFMA operands inside a stage (see slot64 / slot32 / the code runs):
+  // row tile i adds i*4096 (base A) or i*2048 (LoRA A), column tile 1 adds 128 (codes, scales) or
+  // 2048 (LoRA B); those constant parts are immediate offsets inside the step blocks.
+  const uint32_t r = lane & 31, h = lane >> 5;
+  uint32_t off_a64[4], off_a32[2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) off_a64[kk] = r * 128 + ((((2 * kk + h) ^ ((r >> 1) & 7))) << 4);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    off_a32[kk] = (r >> 1) * 128 + (((((r & 1) << 2) | (2 * kk + h)) ^ ((r >> 2) & 7)) << 4);
+  const uint32_t off_codes = kLdsCodes + h * kCodeRun + wave * 256 + r * 4;
+  const uint32_t off_scales = kLdsScales + wave * 256 + r * 4;
+  const uint32_t off_lora_b = kLdsLoraB + wave * 4096;
+  const uint32_t smem0 = lds_addr(smem);
+
+  // prologue: tiles 0..2 in flight; wait for tile 0, then read and decode its first K-step in C++
   issue_tile(c, 0, smem);
   if (total > 1) issue_tile(c, 1, smem + kStage);
-  handover(total > 1 ? 1 : -1, p.k_tiles);
+  if (total > 2) issue_tile(c, 2, smem + 2 * kStage);
+  first_handover(total, p.k_tiles);
 
-  // tile kt is read from stage kt % 3 while tile kt + 2 is copied into stage (kt + 2) % 3
+  bf16x8 aX[8], aY[8], lX[2], lY[2];
+  uint32_t bX[8], bY[8], sdw[2];
+  {
+    const uint8_t* st = smem;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) aX[i] = *reinterpret_cast<const bf16x8*>(st + off_a64[0] + i * 4096);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sdw[j] = *reinterpret_cast<const uint32_t*>(st + off_scales + j * 128);
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(st + off_codes + j * 128);
+      const u32x4 v = nvfp4_dword_to_bf16x8(cw, e4m3_byte_to_f32<0>(sdw[j]));
+      bX[4 * j] = v.x; bX[4 * j + 1] = v.y; bX[4 * j + 2] = v.z; bX[4 * j + 3] = v.w;
+    }
+  }
+
+  // Tile t lives in stage t % 3. Its K-steps 0..2 run, then the handover waits for tile t+1 and
+  // reissues stage t % 3 with tile t+3, and K-step 3 runs while it reads tile t+1's first K-step.
+  // The last base tile and the last LoRA tile are peeled so that the loops carry one step shape.
   int s_cur = 0;
-  for (int kt = 0; kt < p.k_tiles; ++kt) {
-    const int s_next = s_cur >= 1 ? s_cur - 1 : 2;  // (kt + 2) % 3
-    const bool issue = kt + 2 < total;
-    if (issue) issue_tile(c, kt + 2, smem + s_next * kStage);
-    base_tile(smem + s_cur * kStage, lane, ncol, acc);
-    handover(issue ? kt + 2 : -1, p.k_tiles);
-    s_cur = s_cur == 2 ? 0 : s_cur + 1;
+  auto base_steps_012 = [&](uint32_t st) {
+    step_bb(acc, aX, bX, aY, bY, e4m3_byte_to_f32<1>(sdw[0]), e4m3_byte_to_f32<1>(sdw[1]), st + off_a64[1],
+            st + off_codes + 1 * 2 * kCodeRun);
+    step_bb(acc, aY, bY, aX, bX, e4m3_byte_to_f32<2>(sdw[0]), e4m3_byte_to_f32<2>(sdw[1]), st + off_a64[2],
+            st + off_codes + 2 * 2 * kCodeRun);
+    step_bb(acc, aX, bX, aY, bY, e4m3_byte_to_f32<3>(sdw[0]), e4m3_byte_to_f32<3>(sdw[1]), st + off_a64[3],
+            st + off_codes + 3 * 2 * kCodeRun);
+  };
+  auto turn = [&](int kt) {  // handover after tile kt's first steps, then refill its stage
+    handover(kt + 2 < total ? kt + 2 : -1, p.k_tiles);
+    if (kt + 3 < total) issue_tile(c, kt + 3, smem + s_cur * kStage);
+  };
+  int kt = 0;
+  for (; kt + 1 < p.k_tiles; ++kt) {
+    const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+    const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
+    base_steps_012(st);
+    turn(kt);
+    step_bbn(acc, aY, bY, aX, bX, sdw, sn + off_a64[0], sn + off_codes, sn + off_scales);
+    s_cur = s_nxt;
   }
-  for (int kt = p.k_tiles; kt < total; ++kt) {
-    const int s_next = s_cur >= 1 ? s_cur - 1 : 2;
-    const bool issue = kt + 2 < total;
-    if (issue) issue_tile(c, kt + 2, smem + s_next * kStage);
-    lora_tile(smem + s_cur * kStage, lane, ncol, acc);
-    handover(issue ? kt + 2 : -1, p.k_tiles);
-    s_cur = s_cur == 2 ? 0 : s_cur + 1;
+  {  // last base tile
+    const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+    const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
+    base_steps_012(st);
+    turn(kt);
+    if (LORA)
+      step_bl(acc, aY, bY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0]);
+    else
+      step_bn(acc, aY, bY);
+    s_cur = s_nxt;
+    ++kt;
   }
+  if (LORA) {
+    for (; kt + 1 < total; ++kt) {
+      const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+      const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
+      step_ll(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1]);
+      turn(kt);
+      step_ll(acc, aY, lY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0]);
+      s_cur = s_nxt;
+    }
+    const uint32_t st = smem0 + s_cur * kStage;  // last LoRA tile
+    step_ll(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1]);
+    turn(kt);
+    step_ln(acc, aY, lY);
+  }
+  // the last MFMAs must retire before their accumulators are read by ordinary instructions
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // Epilogue. Accumulator register r of lane l in a 32x32 tile holds
   // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
@@ -333,20 +423,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   }
 }
 
-}  // namespace
-
-size_t gemm_w4_lds_bytes() { return kLdsBytes; }
-
-hipError_t launch_gemm_w4(const GemmParams& p0, Epilogue epi, hipStream_t stream) {
-  const void* fn = epi == Epilogue::Plain ? reinterpret_cast<const void*>(&gemm_w4_kernel<0>)
-                                          : reinterpret_cast<const void*>(&gemm_w4_kernel<1>);
-  static std::once_flag once[2];
-  static hipError_t attr_err[2] = {hipSuccess, hipSuccess};
-  const int e = static_cast<int>(epi);
-  std::call_once(once[e], [&] {
-    attr_err[e] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+template <int EPI, bool LORA>
+hipError_t launch_variant(const GemmParams& p0, hipStream_t stream) {
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_w4_kernel<EPI, LORA>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   });
-  if (attr_err[e] != hipSuccess) return attr_err[e];
+  if (attr_err != hipSuccess) return attr_err;
 
   // Buffer offsets are 32-bit: launch row ranges whose activation and t' spans stay below 2 GiB.
   const int64_t row_bytes = std::max<int64_t>(p0.act_ld, p0.lora_t_ld) * 2;
@@ -360,14 +445,21 @@ hipError_t launch_gemm_w4(const GemmParams& p0, Epilogue epi, hipStream_t stream
     p.m_tiles = static_cast<int32_t>((p.S + BM - 1) / BM);
     const int64_t items = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
     const int64_t grid = (items + 7) / 8 * 8;
-    if (epi == Epilogue::Plain)
-      hipLaunchKernelGGL(gemm_w4_kernel<0>, dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
-    else
-      hipLaunchKernelGGL(gemm_w4_kernel<1>, dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
+    hipLaunchKernelGGL((gemm_w4_kernel<EPI, LORA>), dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+size_t gemm_w4_lds_bytes() { return kLdsBytes; }
+
+hipError_t launch_gemm_w4(const GemmParams& p, Epilogue epi, hipStream_t stream) {
+  const bool lora = p.r_tiles > 0;
+  if (epi == Epilogue::Plain) return lora ? launch_variant<0, true>(p, stream) : launch_variant<0, false>(p, stream);
+  return lora ? launch_variant<1, true>(p, stream) : launch_variant<1, false>(p, stream);
 }
 
 }  // namespace h3q

@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--S", type=int, default=37726)
-    ap.add_argument("--cpu-rows", type=int, default=24, help="rows per projection in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=384, help="rows per projection in the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--proj", choices=["qkv", "attn_out", "gate_up", "down"], default=None,
                     help="profiling aid: time one projection only (the JSON line then covers only it)")
@@ -203,7 +203,7 @@ def main():
                    "S": S, "projections": {p.name: [p.N, p.K, p.rank] for p in wl.BLOCK},
                    "weights": "NVFP4 (E2M1 + E4M3/16 + fp32)", "lora": "bf16, rank=alpha, strength 1.0",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_w4_kernel<0>", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": "gemm_w4_kernel<0, true>", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "avg_launch_ms": round(gemm_avg_ms, 4), "launches": gemm_n,
                      "flop_per_launch": gemm_flops_launch, "traffic": None},

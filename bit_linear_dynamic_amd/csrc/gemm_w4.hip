@@ -25,8 +25,9 @@
 // written to LDS. Rows past S lie outside the activation buffer, load as zero and are never stored.
 //
 // Workgroup -> tile order: the hardware hands workgroup b to XCD b % 8; work item w is mapped so that
-// each XCD walks a contiguous range of the (M-tile major, N-tile minor) order, so the workgroups
-// resident on one XCD share one activation M-tile in that XCD's L2 while streaming weight tiles.
+// each XCD walks a contiguous range of a grouped order (pairs of M-tiles sweep the N-tiles together),
+// so the workgroups resident on one XCD share two activation M-tiles in that XCD's L2 and fetch each
+// weight tile once per pair.
 #include <algorithm>
 #include <mutex>
 
@@ -46,6 +47,7 @@ constexpr uint32_t kLdsScales = kLdsCodes + kCodeChunksPerTile * kCodeRun;  // 4
 constexpr uint32_t kLdsLoraB = kLoraTileBytes;           // LoRA tile: B after the 16 KiB t' tile
 constexpr uint32_t kStage = kLdsScales + kScaleTileBytes; // 43008
 constexpr int kStages = 3;
+constexpr int kGroupM = 2;  // row tiles per group in the work order (measured best of 1, 2, 4, 8)
 constexpr uint32_t kLdsBytes = kStages * kStage;         // 129024
 static_assert(kLdsLoraB + kLoraTileBytes <= kStage, "LoRA tile must fit a stage");
 // DMA instructions per wave per K-tile (every wave issues the same number, so that a wave can wait
@@ -239,12 +241,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: keep it scalar
 
-  // XCD-aware work index (gridDim.x is a multiple of 8)
+  // XCD-aware work index (gridDim.x is a multiple of 8; consecutive workgroups go to different
+  // XCDs): each XCD takes one contiguous run of w. Within the run, tiles go in groups of kGroupM row
+  // tiles that sweep all column tiles together, so an XCD's L2 holds two activation row blocks
+  // and each weight column tile is fetched once per pair of row tiles.
   const int per_xcd = gridDim.x >> 3;
   const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (w >= p.m_tiles * p.n_tiles) return;
-  const int mt = __builtin_amdgcn_readfirstlane(w / p.n_tiles);
-  const int nt = __builtin_amdgcn_readfirstlane(w - mt * p.n_tiles);
+  const int grp_items = kGroupM * p.n_tiles;
+  const int grp = w / grp_items, idx = w - grp * grp_items;
+  const int gm = min(kGroupM, p.m_tiles - grp * kGroupM);  // the last group may be short
+  const int mt = __builtin_amdgcn_readfirstlane(grp * kGroupM + idx % gm);
+  const int nt = __builtin_amdgcn_readfirstlane(idx / gm);
   const int64_t m0 = static_cast<int64_t>(mt) * BM;
 
   Ctx c;
@@ -308,10 +316,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   const uint32_t r = lane & 31, h = lane >> 5;
   uint32_t off_a64[4], off_a32[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) off_a64[kk] = r * 128 + ((((2 * kk + h) ^ ((r >> 1) & 7))) << 4);
+  for (int kk = 0; kk < 4; ++kk) off_a64[kk] = slot64(r, 2 * kk + h);
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    off_a32[kk] = (r >> 1) * 128 + (((((r & 1) << 2) | (2 * kk + h)) ^ ((r >> 2) & 7)) << 4);
+  for (int kk = 0; kk < 2; ++kk) off_a32[kk] = slot32(r, 2 * kk + h);
   const uint32_t off_codes = kLdsCodes + h * kCodeRun + wave * 256 + r * 4;
   const uint32_t off_scales = kLdsScales + wave * 256 + r * 4;
   const uint32_t off_lora_b = kLdsLoraB + wave * 4096;

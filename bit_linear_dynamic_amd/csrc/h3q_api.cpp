@@ -7,7 +7,7 @@
 //   W4A4 (H3Q_ACT_NVFP4)          -> activation NVFP4 quantizer first; LoRA-down still reads raw x
 // Selecting or switching an adapter is a host-side map lookup: no device work, and the packed
 // weight is never written.
-#include "../../include/h3q.h"
+#include "h3q.h"
 
 #include <hip/hip_runtime.h>
 

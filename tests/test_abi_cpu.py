@@ -130,3 +130,14 @@ def test_library_does_not_link_the_oracle():
     assert "orc_" not in out
     deps = subprocess.run(["ldd", h3q.LIB_PATH], capture_output=True, text=True).stdout
     assert "oracle" not in deps
+
+
+def test_gemm_steps_inc_is_current():
+    """The inline-asm K-steps the GEMM includes are exactly what their generator writes today."""
+    import importlib.util
+    csrc = os.path.join(ROOT, "bit_linear_dynamic_amd", "csrc")
+    spec = importlib.util.spec_from_file_location("gen_gemm_steps", os.path.join(csrc, "gen_gemm_steps.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    with open(os.path.join(csrc, "gemm_w4_steps.inc")) as f:
+        assert f.read() == gen.render(), "gemm_w4_steps.inc is stale: run csrc/gen_gemm_steps.py"

@@ -55,15 +55,11 @@ static_assert(kLdsLoraB + kLoraTileBytes <= kStage, "LoRA tile must fit a stage"
 constexpr int kCopiesBase = 8 + 2 + 1;  // activation, codes, a quarter of the scales
 constexpr int kCopiesLora = 4 + 4;      // t', B
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-
-// 16 bytes per lane from buffer offset voff + soff to LDS at lds + 16 * lane.
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(lds), 16, voff, soff, 0, 0);
+// Raw buffer descriptor (base, stride 0, size in bytes, gfx950 raw-buffer flags): reads at offsets
+// past `bytes` return zero.
+__device__ __forceinline__ u32x4 rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), gfx9 encoding.
@@ -92,7 +88,7 @@ __device__ __forceinline__ uint32_t slot32(uint32_t row, uint32_t chunk) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 struct Ctx {
-  __amdgpu_buffer_rsrc_t act, lt, codes, scales, lb;
+  u32x4 act, lt, codes, scales, lb;
   // Base tile: copy i (of 8 per wave) fills LDS slots (8w + i)*64 + lane, i.e. tile rows
   // (8w + i)*8 + lane/8; the chunk depends on i only through i & 1, so the per-lane offset is
   // vact[i & 1] plus a uniform (i & ~1) * 8 rows.
@@ -100,32 +96,120 @@ struct Ctx {
   // 128-byte lines (4w + i)*8 + lane/8 holding 16 rows; again the per-lane part depends on i & 1
   // only, and (i & ~1) adds 16 rows per unit.
   uint32_t vact[2], vlt[2], vlb[2];
+  uint32_t lane16;  // lane * 16
   uint32_t act_rows8, lt_rows16;
-  int k_tiles, wave, lane;
+  int k_tiles, total, wave, lane;
 };
 
-// Issues the copies of K-tile kt (base tiles first, then LoRA tiles) into an LDS stage.
-__device__ __forceinline__ void issue_tile(const Ctx& c, int kt, uint8_t* stage) {
-  const int w = c.wave;
-  if (kt < c.k_tiles) {
-    const uint32_t k_bytes = static_cast<uint32_t>(kt) * BK * 2;
+// Copies are issued in windows: the copies of K-tile T are spread over the K-steps between the
+// handover that frees T's stage (that of tile T - 3) and the next handover. A window has 11 copy
+// slots per wave when it spans the four K-steps of a base tile and 8 when it spans two LoRA K-steps:
+//   slots 0..7   the activation tile (a LoRA tile: t' in 0..3, B in 4..7), two slots per 16-row pair
+//   slots 8, 9   the two code runs of this wave's 64 columns
+//   slot 10      this wave's 256 bytes of block scales (lanes 0..15)
+// A LoRA tile in an 11-slot window, and every slot of a window past the last tile, re-read the last
+// base tile's codes and scales (or whole tile) into parts of the stage that nothing reads any more,
+// so every window issues the same number of copies and a handover waits with one vmcnt.
+struct Win {
+  uint32_t g0, g1, g2, g3;   // LDS addresses: slots 0..3 and 4..7 (+1 KiB per slot), 8 (9: + 4 runs), 10
+  uint32_t p[4];             // uniform offsets of slot pairs (0,1), (2,3), (4,5), (6,7)
+  uint32_t p8, p9, p10;
+  u32x4 ra, rb;              // descriptors of slots 0..3 and 4..7
+  uint32_t v[4];             // per-lane offsets: slots 0..3 even/odd, slots 4..7 even/odd
+};
+
+template <bool LORA>
+__device__ __forceinline__ Win plan(const Ctx& c, int T, uint32_t stage) {
+  Win w;
+  const uint32_t wv = static_cast<uint32_t>(c.wave);
+  const uint32_t kb = static_cast<uint32_t>(T < c.k_tiles ? T : c.k_tiles - 1);
+  w.g2 = stage + kLdsCodes + wv * kCodeRun;
+  w.g3 = stage + kLdsScales + wv * 256;
+  w.p8 = kb * kCodeTileBytes + wv * 1024;
+  w.p9 = w.p8 + 4 * 1024;
+  w.p10 = kb * kScaleTileBytes + wv * 256;
+  if (!LORA || T < c.k_tiles || T >= c.total) {  // base tile kb (a harmless re-read past the end)
+    const uint32_t k_bytes = kb * BK * 2;
+    w.g0 = stage + kLdsA + wv * 8192;
+    w.g1 = w.g0 + 4096;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      copy16(c.act, stage + kLdsA + (w * 8 + i) * 1024, c.vact[i & 1], k_bytes + (i & ~1) * c.act_rows8);
-    const uint32_t ct = static_cast<uint32_t>(kt) * kCodeTileBytes;
-    copy16(c.codes, stage + kLdsCodes + w * kCodeRun, c.lane * 16, ct + w * 1024);
-    copy16(c.codes, stage + kLdsCodes + (w + 4) * kCodeRun, c.lane * 16, ct + (w + 4) * 1024);
-    if (c.lane < 16)
-      copy16(c.scales, stage + kLdsScales + w * 256, c.lane * 16,
-             static_cast<uint32_t>(kt) * kScaleTileBytes + w * 256);
+    for (int j = 0; j < 4; ++j) w.p[j] = k_bytes + 2 * j * c.act_rows8;
+    w.ra = c.act;
+    w.rb = c.act;
+    w.v[0] = c.vact[0]; w.v[1] = c.vact[1]; w.v[2] = c.vact[0]; w.v[3] = c.vact[1];
+  } else {  // LoRA tile rt: t' then B
+    const uint32_t rt = static_cast<uint32_t>(T - c.k_tiles);
+    w.g0 = stage + kLdsA + wv * 4096;
+    w.g1 = stage + kLdsLoraB + wv * 4096;
+    w.p[0] = rt * kLoraBK * 2;
+    w.p[1] = w.p[0] + 2 * c.lt_rows16;
+    w.p[2] = rt * kLoraTileBytes;
+    w.p[3] = w.p[2] + 2 * (16 * kLoraBK * 2);
+    w.ra = c.lt;
+    w.rb = c.lb;
+    w.v[0] = c.vlt[0]; w.v[1] = c.vlt[1]; w.v[2] = c.vlb[0]; w.v[3] = c.vlb[1];
+  }
+  return w;
+}
+
+template <int I> __device__ __forceinline__ uint32_t slot_m0(const Win& w) {
+  if constexpr (I < 4) return w.g0 + I * 1024;
+  else if constexpr (I < 8) return w.g1 + (I - 4) * 1024;
+  else if constexpr (I == 8) return w.g2;
+  else if constexpr (I == 9) return w.g2 + 4 * kCodeRun;
+  else return w.g3;
+}
+template <int I> __device__ __forceinline__ uint32_t slot_soff(const Win& w) {
+  if constexpr (I < 8) return w.p[I >> 1];
+  else if constexpr (I == 8) return w.p8;
+  else if constexpr (I == 9) return w.p9;
+  else return w.p10;
+}
+template <int I> __device__ __forceinline__ uint32_t slot_voff(const Ctx& c, const Win& w) {
+  if constexpr (I < 4) return w.v[I & 1];
+  else if constexpr (I < 8) return w.v[2 + (I & 1)];
+  else return c.lane16;
+}
+template <int I> __device__ __forceinline__ u32x4 slot_rsrc(const Ctx& c, const Win& w) {
+  if constexpr (I < 4) return w.ra;
+  else if constexpr (I < 8) return w.rb;
+  else if constexpr (I < 10) return c.codes;
+  else return c.scales;
+}
+
+// Operands of copy j (slot I) of a step block.
+#define H3Q_COPY(j, I)                                                                            \
+  [cm##j] "s"(slot_m0<I>(w)), [cv##j] "v"(slot_voff<I>(c, w)), [cs##j] "s"(slot_soff<I>(w)),      \
+      [cr##j] "s"(slot_rsrc<I>(c, w))
+
+// One copy on its own (prologue). M0 is saved and restored around it.
+template <int I>
+__device__ __forceinline__ void copy_slot(const Ctx& c, const Win& w) {
+  uint32_t msv;
+  if constexpr (I == 10) {
+    uint64_t ex;
+    asm volatile(
+        "s_mov_b32 %[msv], m0\n\ts_mov_b64 %[ex], exec\n\ts_mov_b32 exec_lo, 0xffff\n\ts_mov_b32 exec_hi, 0\n\t"
+        "s_mov_b32 m0, %[cm0]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[cv0], %[cr0], %[cs0] offen lds\n\t"
+        "s_mov_b64 exec, %[ex]\n\ts_mov_b32 m0, %[msv]"
+        : [msv] "=&s"(msv), [ex] "=&s"(ex)
+        : H3Q_COPY(0, I)
+        : "memory");
   } else {
-    const uint32_t rt = static_cast<uint32_t>(kt - c.k_tiles);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      copy16(c.lt, stage + kLdsA + (w * 4 + i) * 1024, c.vlt[i & 1], rt * kLoraBK * 2 + (i & ~1) * c.lt_rows16);
-      copy16(c.lb, stage + kLdsLoraB + (w * 4 + i) * 1024, c.vlb[i & 1],
-             rt * kLoraTileBytes + (i & ~1) * (16 * kLoraBK * 2));
-    }
+    asm volatile(
+        "s_mov_b32 %[msv], m0\n\ts_mov_b32 m0, %[cm0]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[cv0], %[cr0], %[cs0] offen lds\n\ts_mov_b32 m0, %[msv]"
+        : [msv] "=&s"(msv)
+        : H3Q_COPY(0, I)
+        : "memory");
+  }
+}
+
+template <int I, int N>
+__device__ __forceinline__ void copy_slots(const Ctx& c, const Win& w) {
+  if constexpr (N > 0) {
+    copy_slot<I>(c, w);
+    copy_slots<I + 1, N - 1>(c, w);
   }
 }
 
@@ -160,42 +244,66 @@ typedef uint32_t bw_t[8];  // a decoded W4 B operand: 2 column tiles x 4 dwords 
 
 constexpr uint32_t kPermHighHalves = 0x07060302u;  // v_perm_b32: high 16 bits of each source
 
-// base step, next = K-step of the same base tile (scales s0/s1 of that step given)
-__device__ __forceinline__ void step_bb(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
-                                        bw_t& m, float s0, float s1, uint32_t aaddr, uint32_t caddr) {
-  asm volatile(H3Q_STEP_BB_ASM
-               : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m)
+// base step, next = K-step of the same base tile (scales s0/s1 of that step given); copies I..I+2
+template <int I>
+__device__ __forceinline__ void step_bb3(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
+                                         bw_t& m, float s0, float s1, uint32_t aaddr, uint32_t caddr, const Ctx& c,
+                                         const Win& w) {
+  uint32_t msv;
+  asm volatile(H3Q_STEP_BB_C3_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [msv] "=&s"(msv)
                : H3Q_A_IN(a), H3Q_B_IN(b), [s0] "v"(s0), [s1] "v"(s1), [aaddr] "v"(aaddr), [caddr] "v"(caddr),
-                 [sel] "s"(kPermHighHalves)
+                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, I), H3Q_COPY(1, I + 1), H3Q_COPY(2, I + 2)
                : H3Q_STEP_CLOBBERS);
 }
-// base step, next = first K-step of a new base tile (its scale dwords d0/d1 are read here too)
-__device__ __forceinline__ void step_bbn(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
-                                         bw_t& m, uint32_t (&d)[2], uint32_t aaddr, uint32_t caddr, uint32_t saddr) {
-  asm volatile(H3Q_STEP_BBN_ASM
-               : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [d0] "=&v"(d[0]), [d1] "=&v"(d[1])
+// the same with copies 9 and 10 (the scales, lanes 0..15)
+__device__ __forceinline__ void step_bb1m(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
+                                          bw_t& m, float s0, float s1, uint32_t aaddr, uint32_t caddr, const Ctx& c,
+                                          const Win& w) {
+  uint32_t msv;
+  uint64_t ex;
+  asm volatile(H3Q_STEP_BB_C1M_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [msv] "=&s"(msv), [ex] "=&s"(ex)
+               : H3Q_A_IN(a), H3Q_B_IN(b), [s0] "v"(s0), [s1] "v"(s1), [aaddr] "v"(aaddr), [caddr] "v"(caddr),
+                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, 9), H3Q_COPY(1, 10)
+               : H3Q_STEP_CLOBBERS);
+}
+// base step, next = first K-step of a new base tile (its scale dwords d0/d1 are read here too);
+// copies 0..2
+__device__ __forceinline__ void step_bbn3(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
+                                          bw_t& m, uint32_t (&d)[2], uint32_t aaddr, uint32_t caddr, uint32_t saddr,
+                                          const Ctx& c, const Win& w) {
+  uint32_t msv;
+  asm volatile(H3Q_STEP_BBN_C3_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [d0] "=&v"(d[0]), [d1] "=&v"(d[1]), [msv] "=&s"(msv)
                : H3Q_A_IN(a), H3Q_B_IN(b), [aaddr] "v"(aaddr), [caddr] "v"(caddr), [saddr] "v"(saddr),
-                 [sel] "s"(kPermHighHalves)
+                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, 0), H3Q_COPY(1, 1), H3Q_COPY(2, 2)
                : H3Q_STEP_CLOBBERS);
 }
-// base step, next = a LoRA K-step
-__device__ __forceinline__ void step_bl(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
-                                        bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr) {
-  asm volatile(H3Q_STEP_BL_ASM
-               : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1])
-               : H3Q_A_IN(a), H3Q_B_IN(b), [aaddr] "v"(aaddr), [baddr] "v"(baddr)
+// base step, next = a LoRA K-step; copies 0..3
+__device__ __forceinline__ void step_bl4(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b, bf16x8 (&n)[8],
+                                         bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr, const Ctx& c, const Win& w) {
+  uint32_t msv;
+  asm volatile(H3Q_STEP_BL_C4_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [msv] "=&s"(msv)
+               : H3Q_A_IN(a), H3Q_B_IN(b), [aaddr] "v"(aaddr), [baddr] "v"(baddr), H3Q_COPY(0, 0), H3Q_COPY(1, 1),
+                 H3Q_COPY(2, 2), H3Q_COPY(3, 3)
                : H3Q_STEP_CLOBBERS);
 }
 // base step, last of the tile loop
 __device__ __forceinline__ void step_bn(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bw_t& b) {
   asm volatile(H3Q_STEP_BN_ASM : H3Q_ACC(acc) : H3Q_A_IN(a), H3Q_B_IN(b) : H3Q_STEP_CLOBBERS);
 }
-// LoRA step, next = a LoRA K-step
-__device__ __forceinline__ void step_ll(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bf16x8 (&l)[2],
-                                        bf16x8 (&n)[8], bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr) {
-  asm volatile(H3Q_STEP_LL_ASM
-               : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1])
-               : H3Q_A_IN(a), [l0] "v"(l[0]), [l1] "v"(l[1]), [aaddr] "v"(aaddr), [baddr] "v"(baddr)
+// LoRA step, next = a LoRA K-step; copies I..I+3
+template <int I>
+__device__ __forceinline__ void step_ll4(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bf16x8 (&l)[2],
+                                         bf16x8 (&n)[8], bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr, const Ctx& c,
+                                         const Win& w) {
+  uint32_t msv;
+  asm volatile(H3Q_STEP_LL_C4_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [msv] "=&s"(msv)
+               : H3Q_A_IN(a), [l0] "v"(l[0]), [l1] "v"(l[1]), [aaddr] "v"(aaddr), [baddr] "v"(baddr),
+                 H3Q_COPY(0, I), H3Q_COPY(1, I + 1), H3Q_COPY(2, I + 2), H3Q_COPY(3, I + 3)
                : H3Q_STEP_CLOBBERS);
 }
 // LoRA step, last of the tile loop
@@ -206,31 +314,6 @@ __device__ __forceinline__ void step_ln(f32x16 (&acc)[8][2], const bf16x8 (&a)[8
 // LDS byte address of a pointer into the dynamic shared array.
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
-}
-
-// Waits for every copy except those of the newest tile in flight (`newest`, -1 if none), then
-// barriers.
-__device__ __forceinline__ void handover(int newest, int k_tiles) {
-  if (newest < 0)
-    stage_barrier<0>();
-  else if (newest < k_tiles)
-    stage_barrier<kCopiesBase>();
-  else
-    stage_barrier<kCopiesLora>();
-}
-
-// Prologue wait: tile 0 landed while tiles 1 and 2 (if any) stay in flight.
-__device__ __forceinline__ void first_handover(int total, int k_tiles) {
-  const int n1 = total > 1 ? (1 < k_tiles ? kCopiesBase : kCopiesLora) : 0;
-  const int n2 = total > 2 ? (2 < k_tiles ? kCopiesBase : kCopiesLora) : 0;
-  switch (n1 + n2) {
-    case 2 * kCopiesBase: stage_barrier<2 * kCopiesBase>(); break;
-    case kCopiesBase + kCopiesLora: stage_barrier<kCopiesBase + kCopiesLora>(); break;
-    case 2 * kCopiesLora: stage_barrier<2 * kCopiesLora>(); break;
-    case kCopiesBase: stage_barrier<kCopiesBase>(); break;
-    case kCopiesLora: stage_barrier<kCopiesLora>(); break;
-    default: stage_barrier<0>(); break;
-  }
 }
 
 template <int EPI, bool LORA>
@@ -257,8 +340,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
 
   Ctx c;
   c.k_tiles = p.k_tiles;
+  c.total = p.k_tiles + p.r_tiles;
   c.wave = wave;
   c.lane = lane;
+  c.lane16 = lane * 16;
   c.act = rsrc(p.act, static_cast<uint32_t>(p.S * p.act_ld * 2));
   c.codes = rsrc(p.wcodes + static_cast<int64_t>(nt) * p.k_tiles * kCodeTileBytes,
                  static_cast<uint32_t>(p.k_tiles) * kCodeTileBytes);
@@ -324,11 +409,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   const uint32_t off_lora_b = kLdsLoraB + wave * 4096;
   const uint32_t smem0 = lds_addr(smem);
 
-  // prologue: tiles 0..2 in flight; wait for tile 0, then read and decode its first K-step in C++
-  issue_tile(c, 0, smem);
-  if (total > 1) issue_tile(c, 1, smem + kStage);
-  if (total > 2) issue_tile(c, 2, smem + 2 * kStage);
-  first_handover(total, p.k_tiles);
+  // Prologue: tiles 0 and 1 (11 copies each, tile 1 possibly a LoRA tile or a re-read), then the
+  // first three copies of tile 2's window; wait for tile 0, read and decode its first K-step in C++.
+  copy_slots<0, 11>(c, plan<LORA>(c, 0, smem0));
+  copy_slots<0, 11>(c, plan<LORA>(c, 1, smem0 + kStage));
+  Win win = plan<LORA>(c, 2, smem0 + 2 * kStage);
+  copy_slots<0, 3>(c, win);
+  stage_barrier<kCopiesBase + 3>();
 
   bf16x8 aX[8], aY[8], lX[2], lY[2];
   uint32_t bX[8], bY[8], sdw[2];
@@ -345,40 +432,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
     }
   }
 
-  // Tile t lives in stage t % 3. Its K-steps 0..2 run, then the handover waits for tile t+1 and
-  // reissues stage t % 3 with tile t+3, and K-step 3 runs while it reads tile t+1's first K-step.
-  // The last base tile and the last LoRA tile are peeled so that the loops carry one step shape.
+  // Tile t lives in stage t % 3. A base tile runs K-steps 0..2 (carrying copies 3..10 of the
+  // window of tile t + 2), then the handover waits for tile t + 1 and plans tile t + 3 into the
+  // stage t just left, and K-step 3 runs (copies 0..2) while it reads tile t + 1's first K-step.
+  // A LoRA tile runs K-step 0 (copies 4..7), the handover, and K-step 1 (copies 0..3). The last base
+  // tile and the last LoRA tile are peeled so that each loop carries one step shape.
   int s_cur = 0;
   auto base_steps_012 = [&](uint32_t st) {
-    step_bb(acc, aX, bX, aY, bY, e4m3_byte_to_f32<1>(sdw[0]), e4m3_byte_to_f32<1>(sdw[1]), st + off_a64[1],
-            st + off_codes + 1 * 2 * kCodeRun);
-    step_bb(acc, aY, bY, aX, bX, e4m3_byte_to_f32<2>(sdw[0]), e4m3_byte_to_f32<2>(sdw[1]), st + off_a64[2],
-            st + off_codes + 2 * 2 * kCodeRun);
-    step_bb(acc, aX, bX, aY, bY, e4m3_byte_to_f32<3>(sdw[0]), e4m3_byte_to_f32<3>(sdw[1]), st + off_a64[3],
-            st + off_codes + 3 * 2 * kCodeRun);
-  };
-  auto turn = [&](int kt) {  // handover after tile kt's first steps, then refill its stage
-    handover(kt + 2 < total ? kt + 2 : -1, p.k_tiles);
-    if (kt + 3 < total) issue_tile(c, kt + 3, smem + s_cur * kStage);
+    step_bb3<3>(acc, aX, bX, aY, bY, e4m3_byte_to_f32<1>(sdw[0]), e4m3_byte_to_f32<1>(sdw[1]), st + off_a64[1],
+                st + off_codes + 1 * 2 * kCodeRun, c, win);
+    step_bb3<6>(acc, aY, bY, aX, bX, e4m3_byte_to_f32<2>(sdw[0]), e4m3_byte_to_f32<2>(sdw[1]), st + off_a64[2],
+                st + off_codes + 2 * 2 * kCodeRun, c, win);
+    step_bb1m(acc, aX, bX, aY, bY, e4m3_byte_to_f32<3>(sdw[0]), e4m3_byte_to_f32<3>(sdw[1]), st + off_a64[3],
+              st + off_codes + 3 * 2 * kCodeRun, c, win);
   };
   int kt = 0;
   for (; kt + 1 < p.k_tiles; ++kt) {
     const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
     const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
     base_steps_012(st);
-    turn(kt);
-    step_bbn(acc, aY, bY, aX, bX, sdw, sn + off_a64[0], sn + off_codes, sn + off_scales);
+    stage_barrier<kCopiesBase>();  // tile kt+1 has landed; tile kt+2's window may still be in flight
+    win = plan<LORA>(c, kt + 3, st);
+    step_bbn3(acc, aY, bY, aX, bX, sdw, sn + off_a64[0], sn + off_codes, sn + off_scales, c, win);
     s_cur = s_nxt;
   }
   {  // last base tile
     const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
     const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
     base_steps_012(st);
-    turn(kt);
-    if (LORA)
-      step_bl(acc, aY, bY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0]);
-    else
+    if (LORA) {
+      stage_barrier<kCopiesBase>();
+      win = plan<LORA>(c, kt + 3, st);
+      step_bl4(acc, aY, bY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0], c, win);
+    } else {
+      stage_barrier<0>();  // drain every copy before the workgroup can end
       step_bn(acc, aY, bY);
+    }
     s_cur = s_nxt;
     ++kt;
   }
@@ -386,14 +475,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
     for (; kt + 1 < total; ++kt) {
       const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
       const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
-      step_ll(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1]);
-      turn(kt);
-      step_ll(acc, aY, lY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0]);
+      step_ll4<4>(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1], c, win);
+      stage_barrier<kCopiesLora>();
+      win = plan<LORA>(c, kt + 3, st);
+      step_ll4<0>(acc, aY, lY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0], c, win);
       s_cur = s_nxt;
     }
     const uint32_t st = smem0 + s_cur * kStage;  // last LoRA tile
-    step_ll(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1]);
-    turn(kt);
+    step_ll4<4>(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1], c, win);
+    stage_barrier<0>();
     step_ln(acc, aY, lY);
   }
   // the last MFMAs must retire before their accumulators are read by ordinary instructions

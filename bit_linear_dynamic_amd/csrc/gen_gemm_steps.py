@@ -10,6 +10,12 @@ Registers v236..v255 are private to each block (declared clobbered): v240..v247 
 W4 B operand (copied in from the previous block's outputs), v248..v255 are decode temporaries,
 v238/v239 the code dwords, v236/v237 the block scales of a new tile.
 
+A step can also carry global->LDS copies of a later K-tile (buffer_load_dwordx4 ... lds, M0 = LDS
+address), spread between its MFMAs so that the copies of a tile trickle out over the steps between
+two stage handovers instead of leaving every wave at once. Copy j takes operands %[cmj] (M0 value),
+%[cvj] (per-lane offset), %[csj] (uniform offset) and %[crj] (buffer descriptor); a masked copy runs
+on lanes 0..15 only (exec saved in %[ex]). M0 is saved in %[msv] and restored at the end.
+
 Run `python gen_gemm_steps.py` after editing; tests/test_abi_cpu.py checks the .inc is current.
 """
 import os
@@ -35,12 +41,26 @@ def decode_groups(scale_regs):
                         f"v_perm_b32 %[m{4*j+b1}], v{t1+1}, v{t1}, %[sel]"])
     return dec
 
-def step(kind):
+# MFMA positions (0..15) after which the copies of a step go, by copy pattern
+COPY_AT = {"": [], "ccc": [2, 7, 12], "cccc": [1, 5, 9, 13], "cm": [4, 11]}
+
+
+def copy_lines(j, masked):
+    body = [f"s_mov_b32 m0, %[cm{j}]", "s_nop 0", f"buffer_load_dwordx4 %[cv{j}], %[cr{j}], %[cs{j}] offen lds"]
+    if not masked:
+        return body
+    return ["s_mov_b64 %[ex], exec", "s_mov_b32 exec_lo, 0xffff", "s_mov_b32 exec_hi, 0"] + body + \
+           ["s_mov_b64 exec, %[ex]"]
+
+
+def step(kind, copies=""):
     """kind: src ('b' base W4 operand in v240..v247 | 'l' LoRA bf16 operand %[l0],%[l1]) +
     next ('b' next K-step of a base tile | 'B' first K-step of a new base tile (scales read here) |
-          'l' a LoRA K-step | 'n' none)"""
+          'l' a LoRA K-step | 'n' none); copies: one letter per copy, 'c' plain, 'm' lanes 0..15."""
     src, nxt = kind[0], kind[1]
     L = ["s_waitcnt lgkmcnt(0)", "s_nop 3"]
+    if copies:
+        L.append("s_mov_b32 %[msv], m0")
     if src == 'b':
         for q in range(8):
             L.append(f"v_mov_b32 v{240+q}, %[b{q}]")
@@ -65,6 +85,8 @@ def step(kind):
             extras[i].append(f"ds_read_b128 %[n{i}], %[aaddr] offset:{i*2048}")
         extras[8].append("ds_read_b128 %[k0], %[baddr]")
         extras[9].append("ds_read_b128 %[k1], %[baddr] offset:2048")
+    for j, (at, kind_c) in enumerate(zip(COPY_AT[copies], copies)):
+        extras[at] += copy_lines(j, kind_c == 'm')
     L.append("s_nop 1")
     for s in range(16):
         i, j = s // 2, s % 2
@@ -72,17 +94,22 @@ def step(kind):
         L += extras[s]
     if nxt != 'n':
         L.append("s_waitcnt lgkmcnt(0)")
+    if copies:
+        L.append("s_mov_b32 m0, %[msv]")
     return L
 
 def render() -> str:
     out = ["// Generated by gen_gemm_steps.py -- do not edit by hand.",
            "// Step variants: source operand (B = W4 decoded in v240..v247, L = LoRA bf16) x next step",
            "// (B: next K-step of the same base tile, BN: first K-step of a new base tile, L: a LoRA",
-           "// K-step, N: none).", ""]
+           "// K-step, N: none) x copies carried (C3: three, C4: four, C1M: one plus one on lanes 0..15).",
+           ""]
     names = {'bb': 'BB', 'bB': 'BBN', 'bl': 'BL', 'bn': 'BN', 'll': 'LL', 'ln': 'LN'}
-    for kind in ['bb', 'bB', 'bl', 'bn', 'll', 'ln']:
-        out.append(f"#define H3Q_STEP_{names[kind]}_ASM \\")
-        body = step(kind)
+    cnames = {"": "", "ccc": "_C3", "cccc": "_C4", "cm": "_C1M"}
+    for kind, copies in [('bb', 'ccc'), ('bb', 'cm'), ('bB', 'ccc'), ('bl', 'cccc'), ('bn', ''),
+                         ('ll', 'cccc'), ('ln', '')]:
+        out.append(f"#define H3Q_STEP_{names[kind]}{cnames[copies]}_ASM \\")
+        body = step(kind, copies)
         for n, l in enumerate(body):
             out.append(f'  "{l}\\n\\t"' + (" \\" if n + 1 < len(body) else ""))
         out.append("")

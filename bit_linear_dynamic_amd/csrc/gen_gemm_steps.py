@@ -1,14 +1,16 @@
 """Writes gemm_w4_steps.inc: the instruction sequences of one 16-deep K-step of the main GEMM.
 
-A K-step is 16 v_mfma_f32_32x32x16_bf16 (8 row tiles x 2 column tiles of one wave) with the work for
+A K-step is 8 v_mfma_f32_32x32x16_bf16 (4 row tiles x 2 column tiles of one wave) with the work for
 the next K-step spread between them: LDS reads of the next A operand (and codes / scales), and the
 decode of the next 4-bit B operand (E2M1 codes -> fp32 via v_cvt_scalef32_pk_f32_fp4 with scale 1,
 times the E4M3 block scale, packed to bf16 by v_perm_b32). Written as one asm block per step so the
-matrix core is never left waiting behind a run of decode instructions.
+compiler cannot gather the decode into a run that leaves the matrix core idle.
 
-Registers v236..v255 are private to each block (declared clobbered): v240..v247 hold the current
-W4 B operand (copied in from the previous block's outputs), v248..v255 are decode temporaries,
-v238/v239 the code dwords, v236/v237 the block scales of a new tile.
+Registers v108..v111 and v120..v127 are private to each block (declared clobbered): v120..v127 are
+decode temporaries, v110/v111 the code dwords, v108/v109 the block scales of a new tile. They sit at
+the top of the 128 architectural VGPRs a wave has when two waves share a SIMD. The running step's W4
+B operand comes in as two 4-register tuples %[bq0], %[bq1] (the previous block's eight decoded
+outputs, which the compiler allocates in place).
 
 A step can also carry global->LDS copies of a later K-tile (buffer_load_dwordx4 ... lds, M0 = LDS
 address), spread between its MFMAs so that the copies of a tile trickle out over the steps between
@@ -19,30 +21,38 @@ on lanes 0..15 only (exec saved in %[ex]). M0 is saved in %[msv] and restored at
 Run `python gen_gemm_steps.py` after editing; tests/test_abi_cpu.py checks the .inc is current.
 """
 import os
+
+RT = 4          # row tiles (of 32) per wave
+SCL = (108, 109)   # block scales of a new tile (fp32)
+CODE = (110, 111)  # code dwords of the two column tiles
+TMP = 120          # v120..v127: decode temporaries
 SEL = {0: "", 1: " op_sel:[1,0,0]", 2: " op_sel:[0,1,0]", 3: " op_sel:[1,1,0]"}
+
 
 def mf(i, j, b):
     return f"v_mfma_f32_32x32x16_bf16 %[c{i}{j}], %[a{i}], {b}, %[c{i}{j}]"
 
+
 def decode_groups(scale_regs):
-    """Decode codes v238 (scale scale_regs[0]) -> m0..m3 and v239 (scale_regs[1]) -> m4..m7."""
+    """Decode code dword CODE[0] (scale scale_regs[0]) -> m0..m3 and CODE[1] (scale_regs[1]) -> m4..m7."""
     dec = []
-    for j, (w, s) in enumerate([("v238", scale_regs[0]), ("v239", scale_regs[1])]):
+    for j, (w, s) in enumerate([(f"v{CODE[0]}", scale_regs[0]), (f"v{CODE[1]}", scale_regs[1])]):
         for half in range(2):
             b0, b1 = 2 * half, 2 * half + 1
-            t0, t1 = 248 + 4 * half, 250 + 4 * half
+            t0, t1 = TMP + 4 * half, TMP + 2 + 4 * half
             dec.append([f"v_cvt_scalef32_pk_f32_fp4 v[{t0}:{t0+1}], {w}, 1.0{SEL[b0]}",
                         f"v_cvt_scalef32_pk_f32_fp4 v[{t1}:{t1+1}], {w}, 1.0{SEL[b1]}",
                         f"v_mul_f32 v{t0}, {s}, v{t0}",
-                        f"v_mul_f32 v{t0+1}, {s}, v{t0+1}"])
-            dec.append([f"v_mul_f32 v{t1}, {s}, v{t1}",
+                        f"v_mul_f32 v{t0+1}, {s}, v{t0+1}",
+                        f"v_mul_f32 v{t1}, {s}, v{t1}",
                         f"v_mul_f32 v{t1+1}, {s}, v{t1+1}",
                         f"v_perm_b32 %[m{4*j+b0}], v{t0+1}, v{t0}, %[sel]",
                         f"v_perm_b32 %[m{4*j+b1}], v{t1+1}, v{t1}, %[sel]"])
     return dec
 
-# MFMA positions (0..15) after which the copies of a step go, by copy pattern
-COPY_AT = {"": [], "ccc": [2, 7, 12], "cccc": [1, 5, 9, 13], "cm": [4, 11]}
+
+# MFMA positions (0..7) after which the copies of a step go, by copy pattern
+COPY_AT = {"": [], "cc": [1, 5], "ccc": [1, 3, 6], "m": [3]}
 
 
 def copy_lines(j, masked):
@@ -54,43 +64,41 @@ def copy_lines(j, masked):
 
 
 def step(kind, copies=""):
-    """kind: src ('b' base W4 operand in v240..v247 | 'l' LoRA bf16 operand %[l0],%[l1]) +
+    """kind: src ('b' base W4 operand %[bq0],%[bq1] | 'l' LoRA bf16 operand %[l0],%[l1]) +
     next ('b' next K-step of a base tile | 'B' first K-step of a new base tile (scales read here) |
           'l' a LoRA K-step | 'n' none); copies: one letter per copy, 'c' plain, 'm' lanes 0..15."""
     src, nxt = kind[0], kind[1]
     L = ["s_waitcnt lgkmcnt(0)", "s_nop 3"]
     if copies:
         L.append("s_mov_b32 %[msv], m0")
-    if src == 'b':
-        for q in range(8):
-            L.append(f"v_mov_b32 v{240+q}, %[b{q}]")
-    extras = [[] for _ in range(16)]
+    n_mfma = 2 * RT
+    extras = [[] for _ in range(n_mfma)]
     if nxt in 'bB':
         if nxt == 'B':
             L += ["ds_read_b32 %[d0], %[saddr]", "ds_read_b32 %[d1], %[saddr] offset:128"]
-        L += ["ds_read_b32 v238, %[caddr]", "ds_read_b32 v239, %[caddr] offset:128"]
-        for i in range(8):
+        L += [f"ds_read_b32 v{CODE[0]}, %[caddr]", f"ds_read_b32 v{CODE[1]}, %[caddr] offset:128"]
+        for i in range(RT):
             extras[i].append(f"ds_read_b128 %[n{i}], %[aaddr] offset:{i*4096}")
-        extras[7].append("s_waitcnt lgkmcnt(8)")
+        extras[RT - 1].append(f"s_waitcnt lgkmcnt({RT})")
         if nxt == 'B':
-            extras[7] += ["v_cvt_f32_fp8_sdwa v236, %[d0] src0_sel:BYTE_0",
-                          "v_cvt_f32_fp8_sdwa v237, %[d1] src0_sel:BYTE_0"]
-            scales = ("v236", "v237")
+            extras[RT - 1] += [f"v_cvt_f32_fp8_sdwa v{SCL[0]}, %[d0] src0_sel:BYTE_0",
+                               f"v_cvt_f32_fp8_sdwa v{SCL[1]}, %[d1] src0_sel:BYTE_0"]
+            scales = (f"v{SCL[0]}", f"v{SCL[1]}")
         else:
             scales = ("%[s0]", "%[s1]")
         for k, grp in enumerate(decode_groups(scales)):
-            extras[8 + k] += grp
+            extras[RT + k] += grp
     elif nxt == 'l':
-        for i in range(8):
+        for i in range(RT):
             extras[i].append(f"ds_read_b128 %[n{i}], %[aaddr] offset:{i*2048}")
-        extras[8].append("ds_read_b128 %[k0], %[baddr]")
-        extras[9].append("ds_read_b128 %[k1], %[baddr] offset:2048")
+        extras[RT].append("ds_read_b128 %[k0], %[baddr]")
+        extras[RT + 1].append("ds_read_b128 %[k1], %[baddr] offset:2048")
     for j, (at, kind_c) in enumerate(zip(COPY_AT[copies], copies)):
         extras[at] += copy_lines(j, kind_c == 'm')
     L.append("s_nop 1")
-    for s in range(16):
+    for s in range(n_mfma):
         i, j = s // 2, s % 2
-        L.append(mf(i, j, f"v[{240+4*j}:{243+4*j}]" if src == 'b' else f"%[l{j}]"))
+        L.append(mf(i, j, f"%[bq{j}]" if src == 'b' else f"%[l{j}]"))
         L += extras[s]
     if nxt != 'n':
         L.append("s_waitcnt lgkmcnt(0)")
@@ -98,16 +106,17 @@ def step(kind, copies=""):
         L.append("s_mov_b32 m0, %[msv]")
     return L
 
+
 def render() -> str:
     out = ["// Generated by gen_gemm_steps.py -- do not edit by hand.",
-           "// Step variants: source operand (B = W4 decoded in v240..v247, L = LoRA bf16) x next step",
+           "// Step variants: source operand (B = W4 decoded, L = LoRA bf16) x next step",
            "// (B: next K-step of the same base tile, BN: first K-step of a new base tile, L: a LoRA",
-           "// K-step, N: none) x copies carried (C3: three, C4: four, C1M: one plus one on lanes 0..15).",
+           "// K-step, N: none) x copies carried (C2: two, C3: three, M: one on lanes 0..15).",
            ""]
     names = {'bb': 'BB', 'bB': 'BBN', 'bl': 'BL', 'bn': 'BN', 'll': 'LL', 'ln': 'LN'}
-    cnames = {"": "", "ccc": "_C3", "cccc": "_C4", "cm": "_C1M"}
-    for kind, copies in [('bb', 'ccc'), ('bb', 'cm'), ('bB', 'ccc'), ('bl', 'cccc'), ('bn', ''),
-                         ('ll', 'cccc'), ('ln', '')]:
+    cnames = {"": "", "cc": "_C2", "ccc": "_C3", "m": "_M"}
+    for kind, copies in [('bb', 'cc'), ('bb', 'm'), ('bB', 'cc'), ('bl', 'ccc'), ('bn', ''),
+                         ('ll', 'ccc'), ('ln', '')]:
         out.append(f"#define H3Q_STEP_{names[kind]}{cnames[copies]}_ASM \\")
         body = step(kind, copies)
         for n, l in enumerate(body):

@@ -69,5 +69,72 @@ __device__ __forceinline__ u32x4 nvfp4_dword_to_bf16x8(uint32_t cw, float s) {
 __device__ __forceinline__ uint32_t lds_chunk_offset(uint32_t row, uint32_t chunk) {
   return row * 128u + ((chunk ^ ((row >> 1) & 7u)) << 4);
 }
+// ... in a 32-deep tile (64-byte rows): rows are paired into 128-byte lines, then as above.
+__device__ __forceinline__ uint32_t lds_chunk_offset32(uint32_t row, uint32_t chunk) {
+  return lds_chunk_offset(row >> 1, ((row & 1u) << 2) | chunk);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Buffer memory operations written as inline asm, so that the kernels count their vector-memory
+// operations themselves (the compiler neither sees nor waits on them): global->LDS copies
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane to LDS address M0 + 16 * lane) and 16-byte
+// buffer stores. M0 is saved and restored around each copy. A raw buffer descriptor returns zero
+// for reads past its size and drops writes past it.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Copy 16 bytes per lane from buffer offset voff + soff to LDS byte address lds + 16 * lane.
+__device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t msv;
+  asm volatile(
+      "s_mov_b32 %[msv], m0\n\ts_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[r], %[s] offen lds\n\ts_mov_b32 m0, %[msv]"
+      : [msv] "=&s"(msv)
+      : [m] "s"(lds), [v] "v"(voff), [r] "s"(r), [s] "s"(soff)
+      : "memory");
+}
+
+// The same on lanes 0..LANES-1 only.
+template <int LANES>
+__device__ __forceinline__ void dma16_lanes(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  static_assert(LANES > 0 && LANES <= 32, "lane count");
+  uint32_t msv;
+  uint64_t ex;
+  asm volatile(
+      "s_mov_b32 %[msv], m0\n\ts_mov_b64 %[ex], exec\n\ts_mov_b32 exec_lo, %[lm]\n\ts_mov_b32 exec_hi, 0\n\t"
+      "s_mov_b32 m0, %[m]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v], %[r], %[s] offen lds\n\t"
+      "s_mov_b64 exec, %[ex]\n\ts_mov_b32 m0, %[msv]"
+      : [msv] "=&s"(msv), [ex] "=&s"(ex)
+      : [lm] "i"((LANES == 32) ? 0xffffffffu : ((1u << LANES) - 1u)), [m] "s"(lds), [v] "v"(voff), [r] "s"(r),
+        [s] "s"(soff)
+      : "memory");
+}
+
+// Store 16 bytes per lane at buffer offset voff + soff.
+__device__ __forceinline__ void buf_store16(u32x4 data, u32x4 r, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_store_dwordx4 %[d], %[v], %[r], %[s] offen"
+               :
+               : [d] "v"(data), [v] "v"(voff), [r] "s"(r), [s] "s"(soff)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Stage handover: this wave's vector-memory operations except the newest N have completed, its LDS
+// reads have returned, then all waves of the workgroup meet. Written as asm so the compiler adds no
+// fence (a fence would wait for every copy, including tiles still in flight).
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  wait_vmcnt<N>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 }  // namespace h3q

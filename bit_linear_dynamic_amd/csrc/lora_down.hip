@@ -7,11 +7,22 @@
 // The same pass writes the base path's operand xs = bf16(x * pqs) (same section: pre_quant_scale
 // applies to the base path only), since it is already reading every element of x.
 //
-// Geometry: 256 threads (2x2 wave64s), 128 rows of x per workgroup and all r_pad (<= 512) columns,
-// K staged 64 at a time through double-buffered LDS; wave (wm, wn) owns rows wm*64..+64 and
-// columns wn*r_pad/2..+r_pad/2 as 2 x (r_pad/64) tiles of v_mfma_f32_32x32x16_bf16.
+// Geometry: one workgroup of 4 wave64s per CU and RTM row tiles of 32 per workgroup, RTM chosen
+// from S so that the row tiles spread over the CUs in one round. Every wave computes all RTM row
+// tiles for its columns: the r_pad/32 column tiles of 32 go to the waves round-robin, at most NC per
+// wave, as RTM x NC tiles of v_mfma_f32_32x32x16_bf16. x is read once from HBM, so this is a
+// streaming kernel: K is staged 32 at a time through as many LDS stages as fit (up to 8) by
+// buffer->LDS copies of the x tile (RTM*32 x 32), the A tile (r_pad x 32) and 32 pqs values, and the
+// global latency is hidden by the bytes in flight rather than by compute. Each wave waits for its
+// own copies with one vmcnt and a barrier hands the stage over. The waves also write
+// xs = bf16(x * pqs) from the x operand they hold in registers, one 32 x 16 block per store, in
+// turn. Every vector-memory operation of the K loop is issued by the asm helpers of
+// h3q_device.hpp in a fixed number per wave per tile (copies without a real source re-read into a
+// spare LDS area, stores without a real target go past the buffer's end and are dropped), so one
+// vmcnt value per iteration waits exactly for the tile about to be read.
 //
 // Prescale: the elementwise xs = bf16(x * pqs) on its own, for calls without an adapter.
+#include <algorithm>
 #include <mutex>
 
 #include "h3q_device.hpp"
@@ -22,8 +33,29 @@ namespace h3q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = kLoraBM;  // 128
-constexpr int BK = 64;
+constexpr int BK = 32;              // K per stage: 64-byte rows
+constexpr int kMaxRTM = 6;
+constexpr uint32_t kLdsBudget = 150 * 1024;
+
+template <int RTM, int NC>
+struct LdGeo {
+  static constexpr int CT = 4 * NC;                      // column tiles the A stage is sized for
+  static constexpr uint32_t kX = 0;                      // x tile: RTM*32 rows x 64 B
+  static constexpr uint32_t kA = RTM * 32 * BK * 2;      // A tile: CT*32 rows x 64 B
+  static constexpr uint32_t kP = kA + CT * 32 * BK * 2;  // 32 pqs values
+  static constexpr uint32_t kSpare = kP + 256;           // 1 KiB target of padding copies
+  static constexpr uint32_t kStage = kSpare + 1024;
+  static constexpr int kStagesFit = static_cast<int>(kLdsBudget / kStage);
+  static constexpr int kStages = kStagesFit < 8 ? kStagesFit : 8;
+  static constexpr int L = kStages - 1;                  // tiles in flight ahead of the one read
+  static constexpr uint32_t kLds = kStages * kStage;
+  static constexpr int kCopiesX = (2 * RTM + 3) / 4;     // 1 KiB copies per wave (2*RTM per tile)
+  static constexpr int kCopiesA = 2 * NC;                // (at most 2*CT per tile)
+  static constexpr int CPT = kCopiesX + kCopiesA + 1;    // + pqs (2 lanes)
+  static constexpr int NS = (2 * RTM + 3) / 4;           // xs stores per wave per tile (2*RTM)
+  static_assert(kStages >= 3, "at least two tiles in flight");
+  static_assert((L - 1) * CPT + L * NS < 64, "vmcnt range");
+};
 
 // Loads 8 bf16 of x at (row, k) -- zeros past K (K is a multiple of 16, so chunks never straddle).
 __device__ __forceinline__ u32x4 load_x_chunk(const uint16_t* x, int64_t row, int64_t K, int64_t k) {
@@ -31,12 +63,8 @@ __device__ __forceinline__ u32x4 load_x_chunk(const uint16_t* x, int64_t row, in
   return *reinterpret_cast<const u32x4*>(x + row * K + k);
 }
 
-// bf16(x * pqs) for 8 consecutive elements starting at k (pqs null = 1; past K: zero).
-__device__ __forceinline__ u32x4 prescale_chunk(u32x4 xv, const float* pqs, int64_t K, int64_t k) {
-  if (!pqs || k >= K) return xv;
-  const f32x4 p0 = *reinterpret_cast<const f32x4*>(pqs + k);
-  const f32x4 p1 = *reinterpret_cast<const f32x4*>(pqs + k + 4);
-  const float ps[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+// bf16(x * pqs) of 8 consecutive elements (pqs values given).
+__device__ __forceinline__ u32x4 scale_chunk(u32x4 xv, const float (&ps)[8]) {
   u32x4 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -47,104 +75,184 @@ __device__ __forceinline__ u32x4 prescale_chunk(u32x4 xv, const float* pqs, int6
   return out;
 }
 
-template <int RT2>  // r_pad = 64 * RT2
+// bf16(x * pqs) for 8 consecutive elements starting at k (pqs null = 1; past K: zero).
+__device__ __forceinline__ u32x4 prescale_chunk(u32x4 xv, const float* pqs, int64_t K, int64_t k) {
+  if (!pqs || k >= K) return xv;
+  const f32x4 p0 = *reinterpret_cast<const f32x4*>(pqs + k);
+  const f32x4 p1 = *reinterpret_cast<const f32x4*>(pqs + k + 4);
+  const float ps[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+  return scale_chunk(xv, ps);
+}
+
+// Per-lane source offset of 1 KiB copy q of a 32-deep tile whose rows are `row_bytes` apart: the
+// copy fills LDS slots q*64 + lane, 128-byte line L = q*8 + lane/8 holds rows 2L and 2L + 1, and
+// position lane % 8 of the line holds chunk (lane % 8) ^ ((L / 2) % 8) of the pair (bit 2: which
+// row, bits 0..1: which 16 bytes) -- the layout lds_chunk_offset32 reads.
+__device__ __forceinline__ uint32_t copy_src_offset(uint32_t q, uint32_t lane, uint32_t row_bytes) {
+  const uint32_t line = q * 8 + (lane >> 3);
+  const uint32_t cl = (lane & 7) ^ ((line >> 1) & 7);
+  return (line * 2 + (cl >> 2)) * row_bytes + (cl & 3) * 16;
+}
+
+struct LdCtx {
+  u32x4 x, A, pq, xs;
+  uint32_t x_row_bytes, A_row_bytes;
+  uint32_t wave, lane;
+  int k_tiles, x_copies, A_copies;  // real copies per tile for the whole workgroup: 2*RTM, 2*ct
+};
+
+// Issues this wave's copies of K-tile kt (a re-read of the last tile when kt is past the end).
+template <int RTM, int NC>
+__device__ __forceinline__ void issue_tile(const LdCtx& c, int kt, uint32_t stage) {
+  using G = LdGeo<RTM, NC>;
+  const uint32_t k0 = static_cast<uint32_t>(kt < c.k_tiles ? kt : c.k_tiles - 1) * BK;
+#pragma unroll
+  for (int i = 0; i < G::kCopiesX; ++i) {
+    const uint32_t q = c.wave + 4 * i;
+    const bool real = static_cast<int>(q) < c.x_copies;
+    dma16(c.x, stage + (real ? G::kX + q * 1024 : G::kSpare), copy_src_offset(real ? q : 0, c.lane, c.x_row_bytes),
+          k0 * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < G::kCopiesA; ++i) {
+    const uint32_t q = c.wave + 4 * i;
+    const bool real = static_cast<int>(q) < c.A_copies;
+    dma16(c.A, stage + (real ? G::kA + q * 1024 : G::kSpare), copy_src_offset(real ? q : 0, c.lane, c.A_row_bytes),
+          k0 * 2);
+  }
+  dma16_lanes<2>(c.pq, stage + G::kP + c.wave * 32, c.lane * 16, k0 * 4 + c.wave * 32);
+}
+
+// Waits for tile kt: newer than its copies are those of the L - 1 tiles after it and the xs
+// stores of the min(kt, L) iterations since it was issued.
+template <int L, int CPT, int NS>
+__device__ __forceinline__ void wait_tile(int kt) {
+  switch (kt < L ? kt : L) {
+    case 0: stage_barrier<(L - 1) * CPT>(); break;
+    case 1: stage_barrier<(L - 1) * CPT + 1 * NS>(); break;
+    case 2: stage_barrier<(L - 1) * CPT + 2 * NS>(); break;
+    case 3: stage_barrier<(L - 1) * CPT + 3 * NS>(); break;
+    case 4: stage_barrier<(L - 1) * CPT + 4 * NS>(); break;
+    case 5: stage_barrier<(L - 1) * CPT + 5 * NS>(); break;
+    case 6: stage_barrier<(L - 1) * CPT + 6 * NS>(); break;
+    default: stage_barrier<(L - 1) * CPT + 7 * NS>(); break;
+  }
+}
+
+template <int RTM, int NC, bool XS>
 __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p) {
-  constexpr int R = 64 * RT2;
-  constexpr uint32_t kXBytes = BM * BK * 2;       // 16 KiB
-  constexpr uint32_t kABytes = R * BK * 2;        // 8 KiB per 64 ranks
-  constexpr uint32_t kStage = kXBytes + kABytes;
-  constexpr int kAChunks = R * BK / 8 / kThreads; // chunks of A per thread per stage = 2*RT2
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using G = LdGeo<RTM, NC>;
+  constexpr int L = G::L, CPT = G::CPT, NS = XS ? G::NS : 0, NST = G::kStages;
+  constexpr int BM = RTM * 32;
+  static_assert(L <= 7, "wait_tile covers up to 7 tiles in flight");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int k_tiles = static_cast<int>(p.K_pad / BK);
+  const int ct = p.r_pad / 32;  // column tiles: wave w owns tiles w, w + 4, ... (< ct)
 
-  f32x16 acc[2][RT2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < RT2; ++j) acc[i][j] = f32x16{};
+  LdCtx c;
+  c.wave = wave;
+  c.lane = lane;
+  c.k_tiles = static_cast<int>((p.K + BK - 1) / BK);
+  c.x_copies = 2 * RTM;
+  c.A_copies = 2 * ct;
+  c.x_row_bytes = static_cast<uint32_t>(p.K * 2);
+  c.A_row_bytes = static_cast<uint32_t>(p.K_pad * 2);
+  c.x = buf_rsrc(p.x + m0 * p.K, static_cast<uint32_t>(std::min<int64_t>(BM, p.S - m0) * p.K * 2));
+  c.A = buf_rsrc(p.A, static_cast<uint32_t>(int64_t{p.r_pad} * p.K_pad * 2));
+  c.pq = buf_rsrc(p.pqs, p.pqs ? static_cast<uint32_t>(p.K * 4) : 0u);
+  c.xs = buf_rsrc(p.xs_out + m0 * p.K_pad,
+                  XS ? static_cast<uint32_t>(std::min<int64_t>(BM, p.S - m0) * p.K_pad * 2) : 0u);
 
-  u32x4 xr[4], ar[kAChunks];
-  auto load = [&](int kt) {
-    const int64_t k0 = static_cast<int64_t>(kt) * BK;
+  f32x16 acc[RTM][NC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      int64_t row = m0 + (c >> 3);
-      row = row < p.S ? row : p.S - 1;
-      xr[i] = load_x_chunk(p.x, row, p.K, k0 + (c & 7) * 8);
-    }
+  for (int i = 0; i < RTM; ++i)
 #pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int c = tid + kThreads * i;
-      ar[i] = *reinterpret_cast<const u32x4*>(p.A + (c >> 3) * p.K_pad + k0 + (c & 7) * 8);
-    }
-  };
-  auto store = [&](int kt, uint8_t* stage) {
-    const int64_t k0 = static_cast<int64_t>(kt) * BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(stage + lds_chunk_offset(c >> 3, c & 7)) = xr[i];
-      const int64_t row = m0 + (c >> 3);
-      if (p.xs_out && row < p.S) {
-        const int64_t k = k0 + (c & 7) * 8;
-        *reinterpret_cast<u32x4*>(p.xs_out + row * p.K_pad + k) = prescale_chunk(xr[i], p.pqs, p.K, k);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(stage + kXBytes + lds_chunk_offset(c >> 3, c & 7)) = ar[i];
-    }
-  };
+    for (int j = 0; j < NC; ++j) acc[i][j] = f32x16{};
 
-  load(0);
-  store(0, smem);
-  __syncthreads();
+  const uint32_t smem0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(smem)));
+  const uint32_t r32 = lane & 31, h32 = lane >> 5;
 
-  const uint32_t a_row0 = wm * 64 + (lane & 31);
-  const uint32_t b_row0 = wn * (R / 2) + (lane & 31);
-  const uint32_t khalf = lane >> 5;
-  for (int kt = 0; kt < k_tiles; ++kt) {
-    const bool more = kt + 1 < k_tiles;
-    if (more) load(kt + 1);
-    const uint8_t* Xs = smem + (kt & 1) * kStage;
-    const uint8_t* As = Xs + kXBytes;
+#pragma unroll
+  for (int t = 0; t < L; ++t) issue_tile<RTM, NC>(c, t, smem0 + t * G::kStage);
+  int s_cur = 0;
+  for (int kt = 0; kt < c.k_tiles; ++kt) {
+    wait_tile<L, CPT, NS>(kt);
+    const int s_iss = s_cur == 0 ? NST - 1 : s_cur - 1;  // (kt + L) % NST: the stage of tile kt - 1
+    issue_tile<RTM, NC>(c, kt + L, smem0 + s_iss * G::kStage);
+    const uint8_t* st = smem + s_cur * G::kStage;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 a[2], b[RT2];
+      bf16x8 a[RTM], b[NC];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(Xs + lds_chunk_offset(a_row0 + i * 32, kk * 2 + khalf));
+      for (int i = 0; i < RTM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(st + G::kX + lds_chunk_offset32(i * 32 + r32, kk * 2 + h32));
 #pragma unroll
-      for (int j = 0; j < RT2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(As + lds_chunk_offset(b_row0 + j * 32, kk * 2 + khalf));
+      for (int j = 0; j < NC; ++j) {
+        const int jt = static_cast<int>(wave) + 4 * j;
+        b[j] = jt < ct ? *reinterpret_cast<const bf16x8*>(st + G::kA + lds_chunk_offset32(jt * 32 + r32, kk * 2 + h32))
+                       : bf16x8{};
+      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < RTM; ++i)
 #pragma unroll
-        for (int j = 0; j < RT2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NC; ++j)
+          if (static_cast<int>(wave) + 4 * j < ct)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if (XS) {
+        // 32 x 16 blocks (i, kk) in turn: block 2i + kk is stored by wave (2i + kk) % 4
+        float ps[8];
+        if (p.pqs) {
+          const f32x4 q0 = *reinterpret_cast<const f32x4*>(st + G::kP + (kk * 16 + h32 * 8) * 4);
+          const f32x4 q1 = *reinterpret_cast<const f32x4*>(st + G::kP + (kk * 16 + h32 * 8) * 4 + 16);
+          ps[0] = q0.x; ps[1] = q0.y; ps[2] = q0.z; ps[3] = q0.w;
+          ps[4] = q1.x; ps[5] = q1.y; ps[6] = q1.z; ps[7] = q1.w;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) ps[q] = 1.0f;
+        }
+        const uint32_t k = static_cast<uint32_t>(kt) * BK + kk * 16 + h32 * 8;
+#pragma unroll
+        for (int i = 0; i < RTM; ++i) {
+          if ((2 * i + kk) % 4 != static_cast<int>(wave)) continue;
+          u32x4 out = scale_chunk(__builtin_bit_cast(u32x4, a[i]), ps);
+          if (k >= p.K) out = u32x4{0u, 0u, 0u, 0u};  // padding columns [K, K_pad) are zero
+          buf_store16(out, c.xs, (i * 32 + r32) * static_cast<uint32_t>(p.K_pad * 2) + h32 * 16,
+                      (static_cast<uint32_t>(kt) * BK + kk * 16) * 2);
+        }
+      }
     }
-    if (more) store(kt + 1, smem + ((kt + 1) & 1) * kStage);
-    __syncthreads();
+    if (XS) {
+      // pad this wave's stores of the tile to NS with stores past the buffer's end (dropped)
+      int mine = 0;
+#pragma unroll
+      for (int i = 0; i < RTM; ++i)
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) mine += ((2 * i + kk) % 4 == static_cast<int>(wave)) ? 1 : 0;
+#pragma unroll
+      for (int q = 0; q < NS; ++q)
+        if (q >= mine) buf_store16(u32x4{0u, 0u, 0u, 0u}, c.xs, 0x7ffffff0u, 0u);
+    }
+    s_cur = s_cur == NST - 1 ? 0 : s_cur + 1;
   }
+  wait_vmcnt<0>();  // drain the trailing copies and stores before the workgroup can end
 
   const float f = p.f_div_dev ? p.f / *p.f_div_dev : p.f;
-  const int col_lane = lane & 31, row_lane = (lane >> 5) * 4;
+  const int row_lane = (lane >> 5) * 4;
+  const int R = p.r_pad;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RTM; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_lane + (r & 3);
+      const int64_t row = m0 + i * 32 + (r >> 2) * 8 + row_lane + (r & 3);
       if (row >= p.S) continue;
 #pragma unroll
-      for (int j = 0; j < RT2; ++j) {
-        const int col = wn * (R / 2) + j * 32 + col_lane;
-        p.t_out[row * R + col] = static_cast<uint16_t>(f32_to_bf16_rne(f * acc[i][j][r]));
+      for (int j = 0; j < NC; ++j) {
+        const int jt = static_cast<int>(wave) + 4 * j;
+        if (jt < ct) p.t_out[row * R + jt * 32 + r32] = static_cast<uint16_t>(f32_to_bf16_rne(f * acc[i][j][r]));
       }
     }
 }
@@ -161,35 +269,57 @@ __global__ __launch_bounds__(256) void prescale_kernel(PrescaleParams p) {
   }
 }
 
-template <int RT2>
-hipError_t launch_rt(const LoraDownParams& p, hipStream_t stream) {
-  constexpr uint32_t lds = 2 * (BM * BK * 2 + 64 * RT2 * BK * 2);
+template <int RTM, int NC, bool XS>
+hipError_t launch_rt(const LoraDownParams& p, int64_t blocks, hipStream_t stream) {
+  constexpr uint32_t lds = LdGeo<RTM, NC>::kLds;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lora_down_kernel<RT2>),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lora_down_kernel<RTM, NC, XS>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   if (attr_err != hipSuccess) return attr_err;
-  const int64_t grid = (p.S + BM - 1) / BM;
-  hipLaunchKernelGGL(lora_down_kernel<RT2>, dim3(grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((lora_down_kernel<RTM, NC, XS>), dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
+}
+
+template <int RTM, int NC>
+hipError_t launch_x(const LoraDownParams& p, int64_t blocks, hipStream_t stream) {
+  return p.xs_out ? launch_rt<RTM, NC, true>(p, blocks, stream) : launch_rt<RTM, NC, false>(p, blocks, stream);
+}
+
+template <int RTM>
+hipError_t launch_nc(const LoraDownParams& p, int64_t blocks, hipStream_t stream) {
+  switch ((p.r_pad / 32 + 3) / 4) {  // column tiles per wave
+    case 1: return launch_x<RTM, 1>(p, blocks, stream);
+    case 2: return launch_x<RTM, 2>(p, blocks, stream);
+    case 3: return launch_x<RTM, 3>(p, blocks, stream);
+    case 4: return launch_x<RTM, 4>(p, blocks, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream) {
   if (p.S == 0) return hipSuccess;
-  switch (p.r_pad / 64) {
-    case 1: return launch_rt<1>(p, stream);
-    case 2: return launch_rt<2>(p, stream);
-    case 3: return launch_rt<3>(p, stream);
-    case 4: return launch_rt<4>(p, stream);
-    case 5: return launch_rt<5>(p, stream);
-    case 6: return launch_rt<6>(p, stream);
-    case 7: return launch_rt<7>(p, stream);
-    case 8: return launch_rt<8>(p, stream);
-    default: return hipErrorInvalidValue;
+  if (p.r_pad <= 0 || p.r_pad % 64 != 0 || p.r_pad > 512) return hipErrorInvalidValue;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (cus <= 0) return hipErrorInvalidValue;
+  // rows per workgroup: spread the row tiles of 32 over the CUs in one round (at most 6 per CU)
+  const int64_t row_tiles = (p.S + 31) / 32;
+  const int rtm = static_cast<int>(std::min<int64_t>(kMaxRTM, std::max<int64_t>(1, (row_tiles + cus - 1) / cus)));
+  const int64_t blocks = (row_tiles + rtm - 1) / rtm;
+  switch (rtm) {
+    case 1: return launch_nc<1>(p, blocks, stream);
+    case 2: return launch_nc<2>(p, blocks, stream);
+    case 3: return launch_nc<3>(p, blocks, stream);
+    case 4: return launch_nc<4>(p, blocks, stream);
+    case 5: return launch_nc<5>(p, blocks, stream);
+    default: return launch_nc<6>(p, blocks, stream);
   }
 }
 

@@ -27,6 +27,23 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU (published 2.5 PF)
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per GEMM launch of this workload from rocprofv3 FETCH_SIZE (x 2.00) and WRITE_SIZE (x 1.00)
+# counter runs, mean over the four projections (profiles/gemm_w4_block_S37726.md), valid only for the
+# GEMM sources they were taken with (SHA-256 prefix of the files below, in this order).
+GEMM_TRAFFIC_BYTES = 11.486e9
+GEMM_TRAFFIC_SOURCES = ("gemm_w4.hip", "gemm_w4_steps.inc", "h3q_device.hpp", "h3q_kernels.hpp")
+GEMM_TRAFFIC_SHA = "01a9e3bd71284f51"
+
+
+def gemm_traffic():
+    """The counter-derived traffic if the GEMM sources are the ones it was measured on, else None."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "bit_linear_dynamic_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return GEMM_TRAFFIC_BYTES if h.hexdigest()[:16] == GEMM_TRAFFIC_SHA else None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -206,7 +223,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_w4_kernel<0, true>", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "avg_launch_ms": round(gemm_avg_ms, 4), "launches": gemm_n,
-                     "flop_per_launch": gemm_flops_launch, "traffic": None},
+                     "flop_per_launch": gemm_flops_launch, "traffic": gemm_traffic(),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE)"},
         "kernels_ms_per_step": {"gemm": round(gemm_ms / args.steps, 4), "lora_down": round(down_ms / args.steps, 4)},
         "per_projection": per_proj,
         "cpu_baseline": cpu,

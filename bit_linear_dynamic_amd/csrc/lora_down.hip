@@ -11,8 +11,9 @@
 // from S so that the row tiles spread over the CUs in one round. Every wave computes all RTM row
 // tiles for its columns: the r_pad/32 column tiles of 32 go to the waves round-robin, at most NC per
 // wave, as RTM x NC tiles of v_mfma_f32_32x32x16_bf16. x is read once from HBM, so this is a
-// streaming kernel: K is staged 32 at a time through as many LDS stages as fit (up to 8) by
-// buffer->LDS copies of the x tile (RTM*32 x 32), the A tile (r_pad x 32) and 32 pqs values, and the
+// streaming kernel: K is staged BK (64, or 32 when the A tile is large) at a time through as many LDS
+// stages as fit (up to 8) by buffer->LDS copies of the x tile (RTM*32 x BK), the A tile (r_pad x BK)
+// and BK pqs values, and the
 // global latency is hidden by the bytes in flight rather than by compute. Each wave waits for its
 // own copies with one vmcnt and a barrier hands the stage over. The waves also write
 // xs = bf16(x * pqs) from the x operand they hold in registers, one 32 x 16 block per store, in
@@ -33,26 +34,35 @@ namespace h3q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BK = 32;              // K per stage: 64-byte rows
 constexpr int kMaxRTM = 6;
 constexpr uint32_t kLdsBudget = 150 * 1024;
 
+// Stage bytes for K-tiles of depth bk: x tile, A tile, pqs (256 B), 1 KiB target of padding copies.
+constexpr uint32_t ld_stage_bytes(int rtm, int nc, int bk) {
+  return static_cast<uint32_t>(rtm * 32 * bk * 2 + 4 * nc * 32 * bk * 2 + 256 + 1024);
+}
+
 template <int RTM, int NC>
 struct LdGeo {
+  // 64-deep tiles (128-byte row segments) when three stages of them fit, else 32-deep
+  static constexpr int BK = 3 * ld_stage_bytes(RTM, NC, 64) <= kLdsBudget ? 64 : 32;
   static constexpr int CT = 4 * NC;                      // column tiles the A stage is sized for
-  static constexpr uint32_t kX = 0;                      // x tile: RTM*32 rows x 64 B
-  static constexpr uint32_t kA = RTM * 32 * BK * 2;      // A tile: CT*32 rows x 64 B
-  static constexpr uint32_t kP = kA + CT * 32 * BK * 2;  // 32 pqs values
+  static constexpr uint32_t kX = 0;                      // x tile: RTM*32 rows x 2*BK bytes
+  static constexpr uint32_t kA = RTM * 32 * BK * 2;      // A tile: CT*32 rows x 2*BK bytes
+  static constexpr uint32_t kP = kA + CT * 32 * BK * 2;  // BK pqs values
   static constexpr uint32_t kSpare = kP + 256;           // 1 KiB target of padding copies
   static constexpr uint32_t kStage = kSpare + 1024;
   static constexpr int kStagesFit = static_cast<int>(kLdsBudget / kStage);
   static constexpr int kStages = kStagesFit < 8 ? kStagesFit : 8;
   static constexpr int L = kStages - 1;                  // tiles in flight ahead of the one read
   static constexpr uint32_t kLds = kStages * kStage;
-  static constexpr int kCopiesX = (2 * RTM + 3) / 4;     // 1 KiB copies per wave (2*RTM per tile)
-  static constexpr int kCopiesA = 2 * NC;                // (at most 2*CT per tile)
-  static constexpr int CPT = kCopiesX + kCopiesA + 1;    // + pqs (2 lanes)
-  static constexpr int NS = (2 * RTM + 3) / 4;           // xs stores per wave per tile (2*RTM)
+  static constexpr int kCopiesX = (RTM * BK / 16 + 3) / 4;  // 1 KiB copies per wave (RTM*BK/16 per tile)
+  static constexpr int kCopiesA = NC * BK / 16;             // (at most CT*BK/16 per tile)
+  static constexpr int kPqsLanes = BK / 16;                 // 16 bytes each, per wave
+  static constexpr int CPT = kCopiesX + kCopiesA + 1;
+  static constexpr int kBlocks = RTM * (BK / 16);           // 32 x 16 xs blocks per tile
+  static constexpr int NS = (kBlocks + 3) / 4;              // xs stores per wave per tile
+  static_assert(ld_stage_bytes(RTM, NC, BK) == kStage, "stage layout");
   static_assert(kStages >= 3, "at least two tiles in flight");
   static_assert((L - 1) * CPT + L * NS < 64, "vmcnt range");
 };
@@ -84,43 +94,54 @@ __device__ __forceinline__ u32x4 prescale_chunk(u32x4 xv, const float* pqs, int6
   return scale_chunk(xv, ps);
 }
 
-// Per-lane source offset of 1 KiB copy q of a 32-deep tile whose rows are `row_bytes` apart: the
-// copy fills LDS slots q*64 + lane, 128-byte line L = q*8 + lane/8 holds rows 2L and 2L + 1, and
-// position lane % 8 of the line holds chunk (lane % 8) ^ ((L / 2) % 8) of the pair (bit 2: which
-// row, bits 0..1: which 16 bytes) -- the layout lds_chunk_offset32 reads.
+// Per-lane source offset of 1 KiB copy q of a BK-deep tile whose rows are `row_bytes` apart; the
+// copy fills LDS slots q*64 + lane of 128-byte lines, line L = q*8 + lane/8.
+//   BK = 64: line L is row L, position lane % 8 holds chunk (lane % 8) ^ ((L / 2) % 8) -- the
+//            layout lds_chunk_offset reads;
+//   BK = 32: line L holds rows 2L and 2L + 1, position lane % 8 holds chunk (lane % 8) ^ ((L / 2) % 8)
+//            of the pair (bit 2: which row, bits 0..1: which 16 bytes) -- lds_chunk_offset32.
+template <int BK>
 __device__ __forceinline__ uint32_t copy_src_offset(uint32_t q, uint32_t lane, uint32_t row_bytes) {
   const uint32_t line = q * 8 + (lane >> 3);
   const uint32_t cl = (lane & 7) ^ ((line >> 1) & 7);
-  return (line * 2 + (cl >> 2)) * row_bytes + (cl & 3) * 16;
+  if constexpr (BK == 64) return line * row_bytes + cl * 16;
+  else return (line * 2 + (cl >> 2)) * row_bytes + (cl & 3) * 16;
+}
+
+template <int BK>
+__device__ __forceinline__ uint32_t tile_offset(uint32_t row, uint32_t chunk) {
+  if constexpr (BK == 64) return lds_chunk_offset(row, chunk);
+  else return lds_chunk_offset32(row, chunk);
 }
 
 struct LdCtx {
   u32x4 x, A, pq, xs;
   uint32_t x_row_bytes, A_row_bytes;
   uint32_t wave, lane;
-  int k_tiles, x_copies, A_copies;  // real copies per tile for the whole workgroup: 2*RTM, 2*ct
+  int k_tiles, x_copies, A_copies;  // real copies per tile for the whole workgroup
 };
 
 // Issues this wave's copies of K-tile kt (a re-read of the last tile when kt is past the end).
 template <int RTM, int NC>
 __device__ __forceinline__ void issue_tile(const LdCtx& c, int kt, uint32_t stage) {
   using G = LdGeo<RTM, NC>;
+  constexpr int BK = G::BK;
   const uint32_t k0 = static_cast<uint32_t>(kt < c.k_tiles ? kt : c.k_tiles - 1) * BK;
 #pragma unroll
   for (int i = 0; i < G::kCopiesX; ++i) {
     const uint32_t q = c.wave + 4 * i;
     const bool real = static_cast<int>(q) < c.x_copies;
-    dma16(c.x, stage + (real ? G::kX + q * 1024 : G::kSpare), copy_src_offset(real ? q : 0, c.lane, c.x_row_bytes),
+    dma16(c.x, stage + (real ? G::kX + q * 1024 : G::kSpare), copy_src_offset<BK>(real ? q : 0, c.lane, c.x_row_bytes),
           k0 * 2);
   }
 #pragma unroll
   for (int i = 0; i < G::kCopiesA; ++i) {
     const uint32_t q = c.wave + 4 * i;
     const bool real = static_cast<int>(q) < c.A_copies;
-    dma16(c.A, stage + (real ? G::kA + q * 1024 : G::kSpare), copy_src_offset(real ? q : 0, c.lane, c.A_row_bytes),
+    dma16(c.A, stage + (real ? G::kA + q * 1024 : G::kSpare), copy_src_offset<BK>(real ? q : 0, c.lane, c.A_row_bytes),
           k0 * 2);
   }
-  dma16_lanes<2>(c.pq, stage + G::kP + c.wave * 32, c.lane * 16, k0 * 4 + c.wave * 32);
+  dma16_lanes<G::kPqsLanes>(c.pq, stage + G::kP + c.wave * (BK * 1), c.lane * 16, k0 * 4 + c.wave * (BK * 1));
 }
 
 // Waits for tile kt: newer than its copies are those of the L - 1 tiles after it and the xs
@@ -142,7 +163,7 @@ __device__ __forceinline__ void wait_tile(int kt) {
 template <int RTM, int NC, bool XS>
 __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p) {
   using G = LdGeo<RTM, NC>;
-  constexpr int L = G::L, CPT = G::CPT, NS = XS ? G::NS : 0, NST = G::kStages;
+  constexpr int L = G::L, CPT = G::CPT, NS = XS ? G::NS : 0, NST = G::kStages, BK = G::BK;
   constexpr int BM = RTM * 32;
   static_assert(L <= 7, "wait_tile covers up to 7 tiles in flight");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -156,8 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
   c.wave = wave;
   c.lane = lane;
   c.k_tiles = static_cast<int>((p.K + BK - 1) / BK);
-  c.x_copies = 2 * RTM;
-  c.A_copies = 2 * ct;
+  c.x_copies = RTM * BK / 16;
+  c.A_copies = ct * BK / 16;
   c.x_row_bytes = static_cast<uint32_t>(p.K * 2);
   c.A_row_bytes = static_cast<uint32_t>(p.K_pad * 2);
   c.x = buf_rsrc(p.x + m0 * p.K, static_cast<uint32_t>(std::min<int64_t>(BM, p.S - m0) * p.K * 2));
@@ -189,11 +210,11 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
       bf16x8 a[RTM], b[NC];
 #pragma unroll
       for (int i = 0; i < RTM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(st + G::kX + lds_chunk_offset32(i * 32 + r32, kk * 2 + h32));
+        a[i] = *reinterpret_cast<const bf16x8*>(st + G::kX + tile_offset<BK>(i * 32 + r32, kk * 2 + h32));
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int jt = static_cast<int>(wave) + 4 * j;
-        b[j] = jt < ct ? *reinterpret_cast<const bf16x8*>(st + G::kA + lds_chunk_offset32(jt * 32 + r32, kk * 2 + h32))
+        b[j] = jt < ct ? *reinterpret_cast<const bf16x8*>(st + G::kA + tile_offset<BK>(jt * 32 + r32, kk * 2 + h32))
                        : bf16x8{};
       }
 #pragma unroll
@@ -203,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
           if (static_cast<int>(wave) + 4 * j < ct)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       if (XS) {
-        // 32 x 16 blocks (i, kk) in turn: block 2i + kk is stored by wave (2i + kk) % 4
+        // 32 x 16 blocks (i, kk) in turn: block i*(BK/16) + kk is stored by wave (that) % 4
         float ps[8];
         if (p.pqs) {
           const f32x4 q0 = *reinterpret_cast<const f32x4*>(st + G::kP + (kk * 16 + h32 * 8) * 4);
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
         const uint32_t k = static_cast<uint32_t>(kt) * BK + kk * 16 + h32 * 8;
 #pragma unroll
         for (int i = 0; i < RTM; ++i) {
-          if ((2 * i + kk) % 4 != static_cast<int>(wave)) continue;
+          if ((i * (BK / 16) + kk) % 4 != static_cast<int>(wave)) continue;
           u32x4 out = scale_chunk(__builtin_bit_cast(u32x4, a[i]), ps);
           if (k >= p.K) out = u32x4{0u, 0u, 0u, 0u};  // padding columns [K, K_pad) are zero
           buf_store16(out, c.xs, (i * 32 + r32) * static_cast<uint32_t>(p.K_pad * 2) + h32 * 16,
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
 #pragma unroll
       for (int i = 0; i < RTM; ++i)
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) mine += ((2 * i + kk) % 4 == static_cast<int>(wave)) ? 1 : 0;
+        for (int kk = 0; kk < BK / 16; ++kk) mine += ((i * (BK / 16) + kk) % 4 == static_cast<int>(wave)) ? 1 : 0;
 #pragma unroll
       for (int q = 0; q < NS; ++q)
         if (q >= mine) buf_store16(u32x4{0u, 0u, 0u, 0u}, c.xs, 0x7ffffff0u, 0u);
@@ -288,13 +309,23 @@ hipError_t launch_x(const LoraDownParams& p, int64_t blocks, hipStream_t stream)
   return p.xs_out ? launch_rt<RTM, NC, true>(p, blocks, stream) : launch_rt<RTM, NC, false>(p, blocks, stream);
 }
 
+// Row tiles per workgroup allowed with NC column tiles per wave: the RTM x NC accumulator tiles
+// (16 registers each) must stay within the 256 accumulation registers.
+constexpr int max_rtm(int nc) { return nc <= 2 ? kMaxRTM : (nc == 3 ? 5 : 3); }
+
+template <int RTM, int NC>
+hipError_t launch_fit(const LoraDownParams& p, int64_t blocks, hipStream_t stream) {
+  if constexpr (RTM <= max_rtm(NC)) return launch_x<RTM, NC>(p, blocks, stream);
+  else return hipErrorInvalidValue;  // never chosen by launch_lora_down
+}
+
 template <int RTM>
-hipError_t launch_nc(const LoraDownParams& p, int64_t blocks, hipStream_t stream) {
-  switch ((p.r_pad / 32 + 3) / 4) {  // column tiles per wave
-    case 1: return launch_x<RTM, 1>(p, blocks, stream);
-    case 2: return launch_x<RTM, 2>(p, blocks, stream);
-    case 3: return launch_x<RTM, 3>(p, blocks, stream);
-    case 4: return launch_x<RTM, 4>(p, blocks, stream);
+hipError_t launch_nc(const LoraDownParams& p, int nc, int64_t blocks, hipStream_t stream) {
+  switch (nc) {  // column tiles per wave
+    case 1: return launch_fit<RTM, 1>(p, blocks, stream);
+    case 2: return launch_fit<RTM, 2>(p, blocks, stream);
+    case 3: return launch_fit<RTM, 3>(p, blocks, stream);
+    case 4: return launch_fit<RTM, 4>(p, blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -309,17 +340,20 @@ hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (cus <= 0) return hipErrorInvalidValue;
-  // rows per workgroup: spread the row tiles of 32 over the CUs in one round (at most 6 per CU)
+  // rows per workgroup: spread the row tiles of 32 over the CUs in one round (within the register
+  // budget of the column tiles each wave holds)
+  const int nc = (p.r_pad / 32 + 3) / 4;
   const int64_t row_tiles = (p.S + 31) / 32;
-  const int rtm = static_cast<int>(std::min<int64_t>(kMaxRTM, std::max<int64_t>(1, (row_tiles + cus - 1) / cus)));
+  const int rtm = static_cast<int>(
+      std::min<int64_t>(max_rtm(nc), std::max<int64_t>(1, (row_tiles + cus - 1) / cus)));
   const int64_t blocks = (row_tiles + rtm - 1) / rtm;
   switch (rtm) {
-    case 1: return launch_nc<1>(p, blocks, stream);
-    case 2: return launch_nc<2>(p, blocks, stream);
-    case 3: return launch_nc<3>(p, blocks, stream);
-    case 4: return launch_nc<4>(p, blocks, stream);
-    case 5: return launch_nc<5>(p, blocks, stream);
-    default: return launch_nc<6>(p, blocks, stream);
+    case 1: return launch_nc<1>(p, nc, blocks, stream);
+    case 2: return launch_nc<2>(p, nc, blocks, stream);
+    case 3: return launch_nc<3>(p, nc, blocks, stream);
+    case 4: return launch_nc<4>(p, nc, blocks, stream);
+    case 5: return launch_nc<5>(p, nc, blocks, stream);
+    default: return launch_nc<6>(p, nc, blocks, stream);
   }
 }
 

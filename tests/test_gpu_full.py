@@ -158,3 +158,22 @@ def test_w4a4_swiglu_gate_up_s37726(block):
     err = normwise(h.index_select(0, torch.from_numpy(rows).cuda()), oracle.swiglu(y_ref))
     say(f"  h: {len(rows)} sampled rows, normwise={err:.3e}")
     assert err <= TOL
+
+
+def test_rows_beyond_32bit_offsets(block):
+    """The down projection (K = 16384) at S = 65836: the activation spans 2.16 GB, more than the
+    GEMM's 32-bit buffer offsets reach, so the call runs as several row ranges. Rows on both sides
+    of each range boundary and the ragged tail match the oracle, and the first rows are bit-identical
+    to a short call's."""
+    i, p, pr = block["down"]
+    S = 65836
+    say(f"S={S} down, row ranges")
+    x, pqs = inputs(6, i, S, p.K)
+    y = h3q.h3q_linear(x, pqs, pr.handle, 1, 1.0)
+    y_short = h3q.h3q_linear(x[:300].contiguous(), pqs, pr.handle, 1, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:300], y_short)
+    rows_per_launch = ((1 << 31) - 1) // (p.K * 2) // 128 * 128
+    edges = [np.arange(max(0, b - 96), min(S, b + 96)) for b in range(rows_per_launch, S, rows_per_launch)]
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(0, S, 509), np.arange(S - 160, S)] + edges))
+    check_rows(pr, y, x, pqs, rows, 1, 1.0, "adapter 1, strength 1, across row ranges")

@@ -59,6 +59,8 @@ def _declare(lib):
     lib.orc_linear.argtypes = [vp, i64, i64, vp, vp, vp, f32, i64, vp, vp, i64, f64, f64, vp, vp, f32, vp]
     lib.orc_linear.restype = i32
     lib.orc_swiglu.argtypes, lib.orc_swiglu.restype = [vp, i64, i64, vp], None
+    lib.orc_qk_norm_rope.argtypes = [vp, i64, i64, i64, i32, f64, vp, vp, vp, vp, vp]
+    lib.orc_qk_norm_rope.restype = None
     lib.orc_num_threads.argtypes, lib.orc_num_threads.restype = [], i32
     return lib
 
@@ -121,7 +123,8 @@ def prescale_f32(x_bits: np.ndarray, pqs: np.ndarray | None, lib=None) -> np.nda
     x_bits = _c(x_bits, np.uint16)
     rows, K = x_bits.shape
     out = np.empty((rows, K), np.float32)
-    (lib or load()).orc_prescale_f32(_ptr(x_bits), _ptr(_c(pqs, np.float32)), rows, K, _ptr(out))
+    pqs = _c(pqs, np.float32)  # kept alive by the local name across the call
+    (lib or load()).orc_prescale_f32(_ptr(x_bits), _ptr(pqs), rows, K, _ptr(out))
     return out
 
 
@@ -143,10 +146,14 @@ def linear(x_bits, pqs, codes, scales, ts, A_bits=None, B_bits=None, rank=0, alp
     codes = _c(codes, np.uint8)
     N = codes.shape[0]
     y = np.empty((M, N), np.float64)
+    # converted copies must stay referenced until the call returns (a raw pointer keeps nothing alive)
+    pqs, scales = _c(pqs, np.float32), _c(scales, np.uint8)
+    A_bits, B_bits = _c(A_bits, np.uint16), _c(B_bits, np.uint16)
+    act_codes, act_scales = _c(act_codes, np.uint8), _c(act_scales, np.uint8)
     rc = (lib or load()).orc_linear(
-        _ptr(x_bits), M, K, _ptr(_c(pqs, np.float32)), _ptr(codes), _ptr(_c(scales, np.uint8)), float(ts), N,
-        _ptr(_c(A_bits, np.uint16)), _ptr(_c(B_bits, np.uint16)), int(rank), float(alpha), float(strength),
-        _ptr(_c(act_codes, np.uint8)), _ptr(_c(act_scales, np.uint8)), float(ts_a), _ptr(y))
+        _ptr(x_bits), M, K, _ptr(pqs), _ptr(codes), _ptr(scales), float(ts), N,
+        _ptr(A_bits), _ptr(B_bits), int(rank), float(alpha), float(strength),
+        _ptr(act_codes), _ptr(act_scales), float(ts_a), _ptr(y))
     if rc != 0:
         raise ValueError("orc_linear: bad shape")
     return y
@@ -159,6 +166,24 @@ def swiglu(y: np.ndarray, lib=None) -> np.ndarray:
     h = np.empty((M, N2 // 2), np.float64)
     (lib or load()).orc_swiglu(_ptr(y), M, N2 // 2, _ptr(h))
     return h
+
+
+def qk_norm_rope(y: np.ndarray, q_width: int, rot_dim: int, eps: float, gamma_q, gamma_k, cos, sin,
+                 lib=None) -> np.ndarray:
+    """fp64 [M][N] fused-QKV output -> per-head RMSNorm of q and k, then split-half rotation of
+    their first rot_dim dims with the [M][rot_dim/2] angle tables; v unchanged (see oracle.cpp)."""
+    y = _c(y, np.float64)
+    M, N = y.shape
+    if q_width % 128 or 2 * q_width > N or rot_dim % 2 or not 0 <= rot_dim <= 128:
+        raise ValueError("qk_norm_rope: bad q_width or rot_dim")
+    half = rot_dim // 2
+    cos = _c(np.asarray(cos, np.float32).reshape(M, half), np.float32)
+    sin = _c(np.asarray(sin, np.float32).reshape(M, half), np.float32)
+    out = np.empty_like(y)
+    gamma_q, gamma_k = _c(gamma_q, np.float32), _c(gamma_k, np.float32)
+    (lib or load()).orc_qk_norm_rope(_ptr(y), M, N, int(q_width), int(rot_dim), float(eps),
+                                     _ptr(gamma_q), _ptr(gamma_k), _ptr(cos), _ptr(sin), _ptr(out))
+    return out
 
 
 def num_threads(lib=None) -> int:

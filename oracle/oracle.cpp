@@ -235,6 +235,48 @@ void orc_swiglu(const double* y, int64_t M, int64_t F, double* h) {
     }
 }
 
+// Q/K RMSNorm and partial split-half rotary embedding on a fused QKV output (MiniMax-H3 Ultra
+// Fast, "Active optimization stack" (attention projections) and "Kernel path" item 2; which 96 of
+// the 128 head dimensions rotate: MiniMax-H3 Turbo CMF card, "On parity"). y holds M rows of
+// [q (qw) | k (qw) | v (rest)]; q and k are split into heads of 128 consecutive columns. Per row and
+// head, in this order:
+//   1. RMSNorm over the head:  u_i = y_i / sqrt( (1/128) sum_j y_j^2 + eps ) * gamma[head*128 + i]
+//      (gamma_q for q heads, gamma_k for k heads);
+//   2. rotate the first rot dims in split halves: with h = rot/2 and angle table entries
+//      c = cos[m][i], s = sin[m][i] for i < h:
+//        out_i     = u_i * c - u_{i+h} * s
+//        out_{i+h} = u_{i+h} * c + u_i * s
+//      and out_i = u_i for rot <= i < 128.
+// v columns are copied unchanged. cos/sin are [M][rot/2] (the caller's per-token angle table).
+void orc_qk_norm_rope(const double* y, int64_t M, int64_t N, int64_t qw, int32_t rot, double eps,
+                      const float* gamma_q, const float* gamma_k, const float* cos_t, const float* sin_t,
+                      double* out) {
+  const int64_t hd = 128;
+  const int64_t half = rot / 2;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t m = 0; m < M; ++m) {
+    const double* yr = y + m * N;
+    double* orow = out + m * N;
+    for (int64_t n = 0; n < N; ++n) orow[n] = yr[n];
+    for (int64_t c0 = 0; c0 < 2 * qw; c0 += hd) {
+      const float* gamma = c0 < qw ? gamma_q + c0 : gamma_k + (c0 - qw);
+      double ss = 0.0;
+      for (int64_t i = 0; i < hd; ++i) ss += yr[c0 + i] * yr[c0 + i];
+      const double inv = 1.0 / std::sqrt(ss / static_cast<double>(hd) + eps);
+      double u[128];
+      for (int64_t i = 0; i < hd; ++i) u[i] = yr[c0 + i] * inv * static_cast<double>(gamma[i]);
+      for (int64_t i = 0; i < hd; ++i) orow[c0 + i] = u[i];
+      for (int64_t i = 0; i < half; ++i) {
+        const double c = cos_t[m * half + i], s = sin_t[m * half + i];
+        orow[c0 + i] = u[i] * c - u[i + half] * s;
+        orow[c0 + i + half] = u[i + half] * c + u[i] * s;
+      }
+    }
+  }
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

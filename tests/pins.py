@@ -406,4 +406,59 @@ def pin_swiglu(lib):
     assert oracle.swiglu(np.array([[0.0, 3.0]]), lib=lib)[0, 0] == 0.0
 
 
+def _qkv_case(rng, M, heads):
+    """A fused-QKV-shaped output with `heads` heads of 128 in q and in k, and as many columns of v."""
+    qw = 128 * heads
+    y = rng.standard_normal((M, 3 * qw)) * rng.uniform(0.5, 3.0, size=(M, 1))
+    gq, gk = rng.uniform(0.5, 1.5, qw), rng.uniform(0.5, 1.5, qw)
+    return y, qw, gq.astype(np.float32), gk.astype(np.float32)
+
+
+def pin_qk_rmsnorm_vs_linalg(lib):
+    """RMSNorm scope and weights: with no rotation and eps = 0 every 128-column head of q and k is
+    y * sqrt(128) / ||y||_2 * gamma (numpy's norm); v is returned bit for bit; with eps > 0 a
+    constant head c gives c / sqrt(c^2 + eps) * gamma."""
+    rng = np.random.default_rng(29)
+    M = 5
+    y, qw, gq, gk = _qkv_case(rng, M, 2)
+    for rot in (0, 96):
+        half = rot // 2
+        cos, sin = np.ones((M, half), np.float32), np.zeros((M, half), np.float32)
+        got = oracle.qk_norm_rope(y, qw, rot, 0.0, gq, gk, cos, sin, lib=lib)
+        assert np.array_equal(got[:, 2 * qw:], y[:, 2 * qw:])
+        for c0 in range(0, 2 * qw, 128):
+            yh = y[:, c0:c0 + 128]
+            g = (gq[c0:c0 + 128] if c0 < qw else gk[c0 - qw:c0 - qw + 128]).astype(np.float64)
+            want = yh * np.sqrt(128.0) / np.linalg.norm(yh, axis=1, keepdims=True) * g
+            np.testing.assert_allclose(got[:, c0:c0 + 128], want, rtol=1e-13, atol=0)
+    c, eps = 0.75, 0.4375
+    yc = np.full((1, 3 * 128), c)
+    g1 = np.full(128, 2.0, np.float32)
+    got = oracle.qk_norm_rope(yc, 128, 0, eps, g1, g1, np.ones((1, 0)), np.zeros((1, 0)), lib=lib)
+    np.testing.assert_allclose(got[0, :256], c / np.sqrt(c * c + eps) * 2.0, rtol=1e-15)
+
+
+def pin_rope_complex_rotation(lib):
+    """Split-half rotation: dims (i, i + rot/2) of a normalized head form the complex number
+    u_i + j u_{i+rot/2}, multiplied by exp(j theta_i) with theta_i the table's angle (numpy complex
+    arithmetic); dims rot..127 pass through. Checked for rot = 96 (the pages' 96 of 128), 128, 32."""
+    rng = np.random.default_rng(31)
+    M = 4
+    y, qw, gq, gk = _qkv_case(rng, M, 2)
+    for rot in (96, 128, 32):
+        half = rot // 2
+        theta = rng.uniform(-np.pi, np.pi, (M, half))
+        cos, sin = np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+        flat = oracle.qk_norm_rope(y, qw, rot, 1e-6, gq, gk, np.ones((M, half)), np.zeros((M, half)), lib=lib)
+        got = oracle.qk_norm_rope(y, qw, rot, 1e-6, gq, gk, cos, sin, lib=lib)
+        rot_c = cos.astype(np.float64) + 1j * sin.astype(np.float64)
+        for c0 in range(0, 2 * qw, 128):
+            u = flat[:, c0:c0 + 128]
+            z = (u[:, :half] + 1j * u[:, half:rot]) * rot_c
+            np.testing.assert_allclose(got[:, c0:c0 + half], z.real, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(got[:, c0 + half:c0 + rot], z.imag, rtol=1e-12, atol=1e-12)
+            assert np.array_equal(got[:, c0 + rot:c0 + 128], u[:, rot:])
+        assert np.array_equal(got[:, 2 * qw:], y[:, 2 * qw:])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

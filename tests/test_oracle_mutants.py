@@ -46,6 +46,17 @@ MUTANTS = [
     ("silu_sign", "g / (1.0 + std::exp(-g)) * u", "g / (1.0 + std::exp(g)) * u", 0),
     ("gate_up_swapped", "g = y[m * 2 * F + j], u = y[m * 2 * F + F + j]", "u = y[m * 2 * F + j], g = y[m * 2 * F + F + j]", 0),
     ("prescale_f32_no_pqs", "const double p = pqs ? static_cast<double>(pqs[k]) : 1.0;", "const double p = 1.0;", 0),
+    ("rope_sign", "orow[c0 + i] = u[i] * c - u[i + half] * s;", "orow[c0 + i] = u[i] * c + u[i + half] * s;", 0),
+    ("rope_cos_sin_swapped", "const double c = cos_t[m * half + i], s = sin_t[m * half + i];",
+     "const double c = sin_t[m * half + i], s = cos_t[m * half + i];", 0),
+    ("rope_adjacent_pairs", "orow[c0 + i + half] = u[i + half] * c + u[i] * s;",
+     "orow[c0 + i + half] = u[i + half] * c + u[(i + 1) % half] * s;", 0),
+    ("rmsnorm_whole_width", "for (int64_t i = 0; i < hd; ++i) ss += yr[c0 + i] * yr[c0 + i];",
+     "for (int64_t i = 0; i < qw; ++i) ss += yr[(c0 / qw) * qw + i] * yr[(c0 / qw) * qw + i];", 0),
+    ("rmsnorm_eps_outside", "1.0 / std::sqrt(ss / static_cast<double>(hd) + eps)",
+     "1.0 / (std::sqrt(ss / static_cast<double>(hd)) + eps)", 0),
+    ("rmsnorm_gamma_swapped", "c0 < qw ? gamma_q + c0 : gamma_k + (c0 - qw)", "c0 < qw ? gamma_k + c0 : gamma_q + (c0 - qw)", 0),
+    ("rmsnorm_touches_v", "for (int64_t c0 = 0; c0 < 2 * qw; c0 += hd) {", "for (int64_t c0 = 0; c0 < N; c0 += hd) {", 0),
 ]
 
 

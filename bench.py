@@ -196,6 +196,29 @@ def main():
         per_proj[p.name] = {"gemm_ms": round(g / gn, 4), "lora_down_ms": round(l / ln, 4),
                             "gemm_tflops": round(2 * S * p.N * (p.K + p.rank) / (g / gn * 1e-3) / 1e12, 1)}
 
+    # the QKV projection with the fused Q/K RMSNorm + rotary epilogue (48 heads of 128, 96 rotated)
+    qk = None
+    for d in projs:
+        p = d["p"]
+        if p.name != "qkv":
+            continue
+        from bit_linear_dynamic_amd import synth
+        q_width = p.N // 3
+        g = torch.ones(q_width, dtype=torch.float32, device=device)
+        cos, sin = (t.to(device) for t in synth.rope_table(S, 96))
+        h3q.h3q_linear_qk_norm_rope(d["x"], d["pqs"], d["handle"], 1, 1.0, q_width, 96, 1e-6, g, g, cos, sin, y=d["y"])
+        torch.cuda.synchronize()
+        h3q.h3q_timing_enable(True)
+        for _ in range(3):
+            h3q.h3q_linear_qk_norm_rope(d["x"], d["pqs"], d["handle"], 1, 1.0, q_width, 96, 1e-6, g, g, cos, sin,
+                                        y=d["y"])
+        torch.cuda.synchronize()
+        gq, gqn = h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM)
+        h3q.h3q_timing_enable(False)
+        plain = per_proj["qkv"]["gemm_ms"]
+        qk = {"gemm_ms": round(gq / gqn, 4), "plain_gemm_ms": plain,
+              "epilogue_overhead_pct": round(100.0 * (gq / gqn - plain) / plain, 2)}
+
     cpu = None
     if not args.no_cpu:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
@@ -227,6 +250,7 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE)"},
         "kernels_ms_per_step": {"gemm": round(gemm_ms / args.steps, 4), "lora_down": round(down_ms / args.steps, 4)},
         "per_projection": per_proj,
+        "qkv_with_qk_norm_rope": qk,
         "cpu_baseline": cpu,
     }
     for d in projs:

@@ -48,6 +48,7 @@ def _declare(lib):
         "h3q_linear": [vp, vp, i64, vp, vp, i32, f32, vp],
         "h3q_linear_swiglu": [vp, vp, i64, vp, vp, i32, f32, vp],
         "h3q_linear_ex": [vp, vp, i64, vp, vp, i32, f32, u32, vp],
+        "h3q_linear_qk_norm_rope": [vp, vp, i64, vp, vp, i32, f32, u32, i64, i32, f32, vp, vp, vp, vp, vp],
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_dequant": [vp, vp, vp],
         "h3q_weight_checksum": [vp, vp, ctypes.POINTER(ctypes.c_uint64)],
@@ -191,6 +192,38 @@ def h3q_linear(x, pqs, w: int, adapter_id: int, strength: float, y=None, stream=
 
 def h3q_linear_swiglu(x, pqs, w: int, adapter_id: int, strength: float, h=None, stream=None):
     return h3q_linear_ex(x, pqs, w, adapter_id, strength, H3Q_EPI_SWIGLU, h, stream)
+
+
+def h3q_linear_qk_norm_rope(x, pqs, w: int, adapter_id: int, strength: float, q_width: int, rot_dim: int,
+                            eps: float, gamma_q, gamma_k, rope_cos=None, rope_sin=None, flags: int = 0, y=None,
+                            stream=None):
+    """Fused QKV projection + per-head Q/K RMSNorm + split-half rotation of the first rot_dim dims.
+    gamma_q, gamma_k: device fp32 [q_width]; rope_cos, rope_sin: device fp32 [S][rot_dim/2]."""
+    import torch
+    N, K, _ = h3q_weight_info(w)
+    S = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [S][{K}]")
+    if pqs is not None and tuple(pqs.shape) != (K,):
+        raise ValueError(f"pqs must be [{K}]")
+    for name, g in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if tuple(g.shape) != (q_width,):
+            raise ValueError(f"{name} must be [{q_width}]")
+    if rot_dim > 0:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            if t is None or tuple(t.shape) != (S, rot_dim // 2):
+                raise ValueError(f"{name} must be [{S}][{rot_dim // 2}]")
+    if y is None:
+        y = torch.empty((S, N), dtype=torch.bfloat16, device=x.device)
+    elif tuple(y.shape) != (S, N):
+        raise ValueError(f"y must be [{S}][{N}]")
+    _check(lib().h3q_linear_qk_norm_rope(
+        _stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S, _dev_ptr(pqs, torch.float32, "pqs"), ctypes.c_void_p(w),
+        int(adapter_id), float(strength), int(flags), int(q_width), int(rot_dim), float(eps),
+        _dev_ptr(gamma_q, torch.float32, "gamma_q"), _dev_ptr(gamma_k, torch.float32, "gamma_k"),
+        _dev_ptr(rope_cos, torch.float32, "rope_cos"), _dev_ptr(rope_sin, torch.float32, "rope_sin"),
+        _dev_ptr(y, torch.bfloat16, "y")))
+    return y
 
 
 def h3q_quantize_nvfp4(x, pqs=None, stream=None):

@@ -301,6 +301,74 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
+// Q/K tiles of the fused QKV projection (MiniMax-H3 Ultra Fast, "Active optimization stack",
+// attention projections, and "Kernel path" item 2; 96 of 128 head dimensions rotate: MiniMax-H3
+// Turbo CMF card, "On parity"). The tile's 256 columns are two heads of 128. Per row and head:
+//   u_i = v_i / sqrt(mean_j v_j^2 + eps) * gamma_i            (v = ts * acc, fp32)
+//   out_i = u_i c_i - u_{i+h} s_i,  out_{i+h} = u_{i+h} c_i + u_i s_i   (i < h = rot/2)
+//   out_i = u_i                                               (rot <= i < 128)
+// with c, s the caller's per-row angle table. The fp32 tile goes through the freed LDS stages 64 rows
+// at a time ([64][257] floats: one padding float per row keeps a column read by 64 rows on 64
+// banks); then one thread per (row, head) normalizes, rotates in place and stores 16 bytes at a time.
+constexpr int kQkPitch = 257;
+static_assert(64 * kQkPitch * 4 <= kLdsBytes, "Q/K staging must fit the stages");
+
+__device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const f32x16 (&acc)[4][2], uint8_t* smem,
+                                                      float scale, int64_t m0, int nt, int wave, uint32_t lane,
+                                                      bool is_q) {
+  float* tile = reinterpret_cast<float*>(smem);
+  const int tid = threadIdx.x;
+  const float* gamma_tile = is_q ? p.qk_gamma_q + static_cast<int64_t>(nt) * BN
+                                 : p.qk_gamma_k + static_cast<int64_t>(nt - p.q_tiles) * BN;
+  const int half = p.rope_half;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    // every wave is past its last LDS read (pass 0: the last stage handover; pass 1: the barrier
+    // after the row threads below), so the tile can be overwritten
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row_l = ii * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
+          const int col = wave * 64 + j * 32 + static_cast<int>(lane & 31);
+          tile[row_l * kQkPitch + col] = scale * acc[2 * pass + ii][j][r];
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tid < 128) {
+      const int row_l = tid & 63;
+      const int head = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int64_t row = m0 + pass * 64 + row_l;
+      if (row < p.S) {
+        float* t = tile + row_l * kQkPitch + head * 128;
+        const float* g = gamma_tile + head * 128;
+        float ss = 0.0f;
+        for (int i = 0; i < 128; ++i) ss += t[i] * t[i];
+        const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps);
+        const float* cr = p.rope_cos + row * half;
+        const float* sr = p.rope_sin + row * half;
+        for (int i = 0; i < half; ++i) {
+          const float a = t[i] * inv * g[i], b = t[i + half] * inv * g[i + half];
+          const float c = cr[i], s = sr[i];
+          t[i] = a * c - b * s;
+          t[i + half] = b * c + a * s;
+        }
+        for (int i = 2 * half; i < 128; ++i) t[i] = t[i] * inv * g[i];
+        uint16_t* orow = p.out + row * p.out_ld + static_cast<int64_t>(nt) * BN + head * 128;
+        for (int q = 0; q < 16; ++q) {
+          u32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = f32_to_bf16_rne(t[q * 8 + 2 * e]) | (f32_to_bf16_rne(t[q * 8 + 2 * e + 1]) << 16);
+          *reinterpret_cast<u32x4*>(orow + q * 8) = o;
+        }
+      }
+    }
+  }
+}
+
 template <int EPI, bool LORA>
 __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -477,6 +545,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
   // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
   const float scale = p.ts * (p.ts_dev ? *p.ts_dev : 1.0f);
   const int row_lane = (lane >> 5) * 4;
+  if constexpr (EPI == 2) {
+    if (nt < 2 * p.q_tiles) {
+      qk_norm_rope_epilogue(p, acc, smem, scale, m0, nt, wave, lane, nt < p.q_tiles);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -484,7 +558,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
       const int64_t row = m0 + i * 32 + (r >> 2) * 8 + row_lane + (r & 3);
       if (row >= p.S) continue;
       uint16_t* orow = p.out + row * p.out_ld;
-      if (EPI == 0) {
+      if (EPI != 1) {  // plain (also the v columns of the Q/K epilogue)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int cl = static_cast<int>(ncol[j]);
@@ -540,6 +614,8 @@ size_t gemm_w4_lds_bytes() { return kLdsBytes; }
 hipError_t launch_gemm_w4(const GemmParams& p, Epilogue epi, hipStream_t stream) {
   const bool lora = p.r_tiles > 0;
   if (epi == Epilogue::Plain) return lora ? launch_variant<0, true>(p, stream) : launch_variant<0, false>(p, stream);
+  if (epi == Epilogue::QkNormRope)
+    return lora ? launch_variant<2, true>(p, stream) : launch_variant<2, false>(p, stream);
   return lora ? launch_variant<1, true>(p, stream) : launch_variant<1, false>(p, stream);
 }
 

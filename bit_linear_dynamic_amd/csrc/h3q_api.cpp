@@ -399,8 +399,18 @@ h3q_status h3q_list_adapters(h3q_weight w, int32_t* ids, int32_t cap, int32_t* c
   return ok();
 }
 
-h3q_status h3q_linear_ex(void* stream_, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
-                         int32_t adapter_id, float strength, uint32_t flags, uint16_t* out) {
+namespace {
+
+// Arguments of the Q/K RMSNorm + rotary epilogue (h3q_linear_qk_norm_rope).
+struct QkArgs {
+  int64_t q_width;
+  int32_t rot_dim;
+  float eps;
+  const float *gamma_q, *gamma_k, *cos, *sin;
+};
+
+h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                       int32_t adapter_id, float strength, uint32_t flags, uint16_t* out, const QkArgs* qk) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (!live(w)) return fail(H3Q_E_ARG, "linear: not a live weight handle");
   if (S != 0 && (!x || !out)) return fail(H3Q_E_ARG, "linear: null x or output");
@@ -488,10 +498,48 @@ h3q_status h3q_linear_ex(void* stream_, const uint16_t* x, int64_t S, const floa
   g.ts_dev = w4a4 ? ts_a : nullptr;
   g.out = out;
   g.out_ld = n_out;
-  e = timed(H3Q_KERNEL_GEMM, stream,
-            [&] { return launch_gemm_w4(g, swiglu ? Epilogue::SwiGLU : Epilogue::Plain, stream); });
+  Epilogue epi = swiglu ? Epilogue::SwiGLU : Epilogue::Plain;
+  if (qk) {
+    g.qk_gamma_q = qk->gamma_q;
+    g.qk_gamma_k = qk->gamma_k;
+    g.rope_cos = qk->cos;
+    g.rope_sin = qk->sin;
+    g.q_tiles = static_cast<int32_t>(qk->q_width / kGemmBN);
+    g.rope_half = qk->rot_dim / 2;
+    g.qk_eps = qk->eps;
+    epi = Epilogue::QkNormRope;
+  }
+  e = timed(H3Q_KERNEL_GEMM, stream, [&] { return launch_gemm_w4(g, epi, stream); });
   if (e != hipSuccess) return fail(H3Q_E_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+h3q_status h3q_linear_ex(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                         int32_t adapter_id, float strength, uint32_t flags, uint16_t* out) {
+  return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags, out, nullptr);
+}
+
+h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                                   int32_t adapter_id, float strength, uint32_t flags, int64_t q_width,
+                                   int32_t rot_dim, float eps, const float* gamma_q, const float* gamma_k,
+                                   const float* rope_cos, const float* rope_sin, uint16_t* y) {
+  if (!live(w)) return fail(H3Q_E_ARG, "qk_norm_rope: not a live weight handle");
+  if ((flags & ~static_cast<uint32_t>(H3Q_ACT_NVFP4)) != 0)
+    return fail(H3Q_E_ARG, "qk_norm_rope: only H3Q_ACT_NVFP4 may be set (got flags 0x%x)", flags);
+  if (gate_up(w)) return fail(H3Q_E_ARG, "qk_norm_rope: the weight is packed as gate/up");
+  if (q_width <= 0 || q_width % kGemmBN != 0 || 2 * q_width > w->N || w->N % 8 != 0)
+    return fail(H3Q_E_SHAPE, "qk_norm_rope: need q_width a positive multiple of %d, 2*q_width <= N, N %% 8 == 0",
+                kGemmBN);
+  if (rot_dim < 0 || rot_dim > 128 || rot_dim % 2 != 0)
+    return fail(H3Q_E_SHAPE, "qk_norm_rope: rot_dim must be even and in [0, 128] (got %d)", rot_dim);
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(H3Q_E_ARG, "qk_norm_rope: eps must be finite and > 0");
+  if (!gamma_q || !gamma_k || (rot_dim > 0 && (!rope_cos || !rope_sin)))
+    return fail(H3Q_E_ARG, "qk_norm_rope: null gamma or angle table");
+  if (S != 0 && !aligned16(y)) return fail(H3Q_E_ARG, "qk_norm_rope: y must be 16-byte aligned");
+  const QkArgs qk{q_width, rot_dim, eps, gamma_q, gamma_k, rope_cos, rope_sin};
+  return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags, y, &qk);
 }
 
 h3q_status h3q_linear(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,

@@ -40,9 +40,17 @@ struct GemmParams {
   const float* ts_dev;      // optional device scalar multiplying ts (W4A4 activation scale)
   uint16_t* out;            // bf16 [S][n_out]
   int64_t out_ld;
+  // Q/K RMSNorm + rotary epilogue only: column tiles [0, q_tiles) are q, [q_tiles, 2 q_tiles) are k
+  const float* qk_gamma_q;  // fp32 [q_tiles * 256]
+  const float* qk_gamma_k;  // fp32 [q_tiles * 256]
+  const float* rope_cos;    // fp32 [S][rope_half]
+  const float* rope_sin;    // fp32 [S][rope_half]
+  int32_t q_tiles;
+  int32_t rope_half;        // rotated pairs per 128-wide head (rot_dim / 2)
+  float qk_eps;
 };
 
-enum class Epilogue { Plain = 0, SwiGLU = 1 };
+enum class Epilogue { Plain = 0, SwiGLU = 1, QkNormRope = 2 };
 
 hipError_t launch_gemm_w4(const GemmParams& p, Epilogue epi, hipStream_t stream);
 size_t gemm_w4_lds_bytes();

@@ -72,3 +72,26 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 def from_bf16_bits(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def rope_table(S: int, rot_dim: int, frame_hw=(48, 84), base: float = 10000.0, device="cpu"):
+    """Per-token rotary angle table for a packed video sequence (the caller-side input of the Q/K
+    RMSNorm + rotary epilogue): token s sits at (t, h, w) of a grid of frames of frame_hw latent
+    cells (48 x 84: a 768 x 1344 canvas at 16 pixels per cell), and the rot_dim/2 rotated pairs are
+    split evenly over the three axes, pair j of an axis turning at base^(-j/n) per position step
+    (n pairs per axis). Returns (cos, sin) fp32 [S][rot_dim/2]."""
+    half = rot_dim // 2
+    s = torch.arange(S, dtype=torch.float64)
+    H, W = frame_hw
+    pos = torch.stack([torch.div(s, H * W, rounding_mode="floor"),
+                       torch.remainder(torch.div(s, W, rounding_mode="floor"), H),
+                       torch.remainder(s, W)], dim=1)                          # [S][3]
+    per_axis = [half // 3 + (1 if a < half % 3 else 0) for a in range(3)]
+    cols = []
+    for a, n in enumerate(per_axis):
+        if n == 0:
+            continue
+        freq = base ** (-torch.arange(n, dtype=torch.float64) / n)
+        cols.append(pos[:, a:a + 1] * freq[None, :])
+    theta = torch.cat(cols, dim=1) if cols else torch.zeros((S, 0), dtype=torch.float64)
+    return theta.cos().float().to(device), theta.sin().float().to(device)

@@ -116,6 +116,27 @@ h3q_status h3q_linear_swiglu(void* stream, const uint16_t* x, int64_t S, const f
 h3q_status h3q_linear_ex(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
                          int32_t adapter_id, float strength, uint32_t flags, uint16_t* out);
 
+/* Fused QKV projection followed by per-head Q/K RMSNorm and partial split-half rotary embedding
+ * (MiniMax-H3 Ultra Fast, "Active optimization stack", attention projections: one fused QKV matrix
+ * and one fused in-place Q/K RMSNorm + partial split-half RoPE; "Kernel path", item 2; 96 of the 128
+ * head dimensions rotate: MiniMax-H3 Turbo CMF card, "On parity"). The projection is h3q_linear_ex
+ * (flags: 0 or H3Q_ACT_NVFP4); its output columns are [q: q_width | k: q_width | v: the rest], q and
+ * k in heads of 128. For each row and each q or k head, with v = the projection's fp32 value:
+ *   u_i       = v_i / sqrt(mean_j v_j^2 + eps) * gamma_i        (gamma_q for q heads, gamma_k for k)
+ *   y_i       = u_i * c_i - u_{i+h} * s_i,  y_{i+h} = u_{i+h} * c_i + u_i * s_i    (i < h = rot_dim/2)
+ *   y_i       = u_i                                              (rot_dim <= i < 128)
+ * with c = rope_cos[row][i], s = rope_sin[row][i]; v columns are the plain projection.
+ *   q_width   multiple of 256 with 2 * q_width <= N (N a multiple of 8); weight not gate/up
+ *   rot_dim   even, 0..128                  eps  finite, > 0
+ *   gamma_q, gamma_k  device fp32 [q_width]
+ *   rope_cos, rope_sin  device fp32 [S][rot_dim/2] (may be NULL when rot_dim is 0)
+ *   y         device bf16 [S][N], 16-byte aligned, must not overlap x
+ * Otherwise as h3q_linear. */
+h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                                   int32_t adapter_id, float strength, uint32_t flags, int64_t q_width,
+                                   int32_t rot_dim, float eps, const float* gamma_q, const float* gamma_k,
+                                   const float* rope_cos, const float* rope_sin, uint16_t* y);
+
 /* The W4A4 activation quantizer on its own (MiniMax-H3 Ultra Fast, "Kernel path", item 1), as
  * h3q_linear_ex(H3Q_ACT_NVFP4) runs it:
  *   v      = f32(x) * pqs[k] rounded to fp32            (pqs NULL -> v = x)

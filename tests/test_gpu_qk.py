@@ -1,0 +1,145 @@
+"""The fused QKV projection with per-head Q/K RMSNorm and partial split-half rotary embedding
+(MiniMax-H3 Ultra Fast, "Active optimization stack" and "Kernel path"; 96 of 128 head dimensions
+rotate: MiniMax-H3 Turbo CMF card, "On parity") against the fp64 oracle: small and ragged shapes,
+the W4A4 activation path, the full QKV shape, and argument errors. The v columns must equal the plain
+projection's output bit for bit (same GEMM, plain store)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_linear_dynamic_amd as h3q
+import oracle
+from bit_linear_dynamic_amd import synth
+from bit_linear_dynamic_amd import workloads as wl
+from gpu_helpers import TOL, Proj, bits, normwise, say
+
+pytestmark = pytest.mark.gpu
+
+NONE = h3q.H3Q_ADAPTER_NONE
+EPS = 1e-6
+
+
+@pytest.fixture(autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def gammas(q_width, seed):
+    g = synth.uniform((2, q_width), 0.5, 1.5, seed)
+    return g[0].contiguous(), g[1].contiguous()
+
+
+def run_case(p: Proj, x, pqs, q_width, rot, adapter_id, strength, flags=0, rows=None):
+    S = x.shape[0]
+    gq, gk = gammas(q_width, 900 + q_width + rot)
+    cos, sin = synth.rope_table(S, rot)
+    dev = "cuda"
+    y = h3q.h3q_linear_qk_norm_rope(x.to(dev), pqs.to(dev) if pqs is not None else None, p.handle, adapter_id,
+                                    strength, q_width, rot, EPS, gq.to(dev), gk.to(dev),
+                                    cos.to(dev) if rot else None, sin.to(dev) if rot else None, flags=flags)
+    plain = h3q.h3q_linear_ex(x.to(dev), pqs.to(dev) if pqs is not None else None, p.handle, adapter_id, strength,
+                              flags)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, 2 * q_width:], plain[:, 2 * q_width:]), "v columns differ from the plain projection"
+    sel = np.arange(S) if rows is None else rows
+    xb = bits(x[torch.from_numpy(sel)])
+    pq = pqs.numpy() if pqs is not None else None
+    lin = p.reference(xb, pq, adapter_id, strength, w4a4=bool(flags & h3q.H3Q_ACT_NVFP4)) if rows is None else None
+    if rows is not None:  # W4A4 is not run on row samples (its activation scale spans all rows)
+        lin = p.reference(xb, pq, adapter_id, strength)
+    ref = oracle.qk_norm_rope(lin, q_width, rot, EPS, gq.numpy(), gk.numpy(), cos.numpy()[sel], sin.numpy()[sel])
+    ys = y.index_select(0, torch.from_numpy(sel).cuda())
+    eq = normwise(ys[:, :q_width], ref[:, :q_width])
+    ek = normwise(ys[:, q_width:2 * q_width], ref[:, q_width:2 * q_width])
+    ev = normwise(ys[:, 2 * q_width:], ref[:, 2 * q_width:])
+    say(f"  q {eq:.3e}  k {ek:.3e}  v {ev:.3e}")
+    assert max(eq, ek, ev) <= TOL
+    return y
+
+
+CASES = [
+    # S, K, q_width, v width (0: q_width), rot_dim, rank
+    (300, 512, 256, 0, 96, 64),
+    (37, 208, 256, 104, 96, 16),
+    (129, 256, 512, 0, 128, 64),
+    (64, 320, 256, 0, 0, 64),
+    (513, 1024, 768, 0, 96, 384),
+]
+
+
+@pytest.mark.parametrize("S,K,q_width,extra,rot,rank", CASES)
+def test_qk_norm_rope_parity(S, K, q_width, extra, rot, rank):
+    N = 2 * q_width + (extra or q_width)  # a narrower v ends in a ragged column tile
+    say(f"qk S={S} K={K} q_width={q_width} N={N} rot={rot} r={rank}")
+    p = Proj(N, K, 1100 + S + K)
+    try:
+        p.add_adapter(1, rank, float(rank) / 2, 1101, 1102)
+        x = synth.activation(S, K, 1103)
+        pqs = synth.pre_quant_scale(K, 1104)
+        for aid, st in ((NONE, 0.0), (1, 1.0)):
+            run_case(p, x, pqs, q_width, rot, aid, st)
+    finally:
+        p.free()
+
+
+def test_qk_norm_rope_w4a4():
+    S, K, q_width = 200, 512, 256
+    say("qk W4A4")
+    p = Proj(3 * q_width, K, 1200)
+    try:
+        p.add_adapter(1, 64, 64.0, 1201, 1202)
+        run_case(p, synth.activation(S, K, 1203), synth.pre_quant_scale(K, 1204), q_width, 96, 1, 1.0,
+                 flags=h3q.H3Q_ACT_NVFP4)
+    finally:
+        p.free()
+
+
+@pytest.mark.slow
+def test_qk_norm_rope_full_qkv_s8192():
+    """The block's fused QKV projection (18432 x 6144, 48 heads each of q, k, v, rank 384) at S = 8192
+    on sampled rows (first 256, last 256, every 128th)."""
+    S, P = wl.S_MID, wl.QKV
+    say(f"qk full QKV S={S}")
+    p = Proj(P.N, P.K, synth.seed_of(2, 0, synth.W))
+    try:
+        p.add_adapter(1, P.rank, P.alpha, synth.seed_of(2, 0, synth.A1), synth.seed_of(2, 0, synth.B1))
+        x = synth.activation(S, P.K, synth.seed_of(7, 0, synth.X))
+        pqs = synth.pre_quant_scale(P.K, synth.seed_of(7, 0, synth.PQS))
+        rows = np.unique(np.concatenate([np.arange(256), np.arange(256, S - 256, 128), np.arange(S - 256, S)]))
+        run_case(p, x, pqs, wl.D_MODEL, 96, 1, 1.0, rows=rows)
+    finally:
+        p.free()
+
+
+def test_qk_norm_rope_argument_errors():
+    K, q_width = 64, 256
+    p = Proj(3 * q_width, K, 1300)
+    gu = Proj(2 * 256, K, 1301, gate_up=True)
+    try:
+        x = synth.activation(4, K, 1302).cuda()
+        g = torch.ones(q_width, device="cuda")
+        cos, sin = (t.cuda() for t in synth.rope_table(4, 96))
+        ok = dict(q_width=q_width, rot_dim=96, eps=EPS, gamma_q=g, gamma_k=g, rope_cos=cos, rope_sin=sin)
+
+        def expect(code, handle=p.handle, **kw):
+            args = dict(ok, **kw)
+            flags = args.pop("flags", 0)
+            with pytest.raises(h3q.H3QError) as e:
+                h3q.h3q_linear_qk_norm_rope(x, None, handle, NONE, 0.0, flags=flags, **args)
+            assert e.value.code == code, (kw, e.value)
+
+        expect(h3q.H3Q_E_SHAPE, q_width=128, gamma_q=g[:128].contiguous(), gamma_k=g[:128].contiguous())
+        expect(h3q.H3Q_E_SHAPE, q_width=512, gamma_q=torch.ones(512, device="cuda"),
+               gamma_k=torch.ones(512, device="cuda"))
+        expect(h3q.H3Q_E_SHAPE, rot_dim=97, rope_cos=cos[:, :48].contiguous(), rope_sin=sin[:, :48].contiguous())
+        expect(h3q.H3Q_E_ARG, eps=0.0)
+        expect(h3q.H3Q_E_ARG, eps=float("nan"))
+        expect(h3q.H3Q_E_ARG, flags=h3q.H3Q_EPI_SWIGLU)
+        expect(h3q.H3Q_E_ARG, handle=gu.handle, q_width=256)
+        expect(h3q.H3Q_E_ARG, flags=1 << 7)
+    finally:
+        p.free()
+        gu.free()

@@ -309,7 +309,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 //   out_i = u_i                                               (rot <= i < 128)
 // with c, s the caller's per-row angle table. The fp32 tile goes through the freed LDS stages 64 rows
 // at a time ([64][257] floats: one padding float per row keeps a column read by 64 rows on 64
-// banks); then one thread per (row, head) normalizes, rotates in place and stores 16 bytes at a time.
+// banks); then two threads per (row, head) normalize and rotate in place, and store 16 bytes at a
+// time.
 constexpr int kQkPitch = 257;
 static_assert(64 * kQkPitch * 4 <= kLdsBytes, "Q/K staging must fit the stages");
 
@@ -337,33 +338,64 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
           tile[row_l * kQkPitch + col] = scale * acc[2 * pass + ii][j][r];
         }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (tid < 128) {
-      const int row_l = tid & 63;
-      const int head = __builtin_amdgcn_readfirstlane(tid >> 6);
-      const int64_t row = m0 + pass * 64 + row_l;
-      if (row < p.S) {
-        float* t = tile + row_l * kQkPitch + head * 128;
-        const float* g = gamma_tile + head * 128;
-        float ss = 0.0f;
-        for (int i = 0; i < 128; ++i) ss += t[i] * t[i];
-        const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps);
-        const float* cr = p.rope_cos + row * half;
-        const float* sr = p.rope_sin + row * half;
-        for (int i = 0; i < half; ++i) {
-          const float a = t[i] * inv * g[i], b = t[i + half] * inv * g[i + half];
-          const float c = cr[i], s = sr[i];
-          t[i] = a * c - b * s;
-          t[i + half] = b * c + a * s;
-        }
-        for (int i = 2 * half; i < 128; ++i) t[i] = t[i] * inv * g[i];
-        uint16_t* orow = p.out + row * p.out_ld + static_cast<int64_t>(nt) * BN + head * 128;
-        for (int q = 0; q < 16; ++q) {
-          u32x4 o;
+    // Two threads per (row, head): part 0 takes the first half of the rotated pairs and of the
+    // pass-through dims, part 1 the second; both compute the head's sum of squares.
+    const int job = tid & 127, part = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int row_l = job & 63;
+    const int head = __builtin_amdgcn_readfirstlane(job >> 6);
+    const int64_t row = m0 + pass * 64 + row_l;
+    float* t = tile + row_l * kQkPitch + head * 128;
+    float inv = 0.0f;
+    if (row < p.S) {
+      float ss = 0.0f;
+#pragma unroll 16
+      for (int i = 0; i < 128; ++i) ss += t[i] * t[i];
+      inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps);
+    }
+    // both parts have read the whole head before either rewrites its half
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (row < p.S) {
+      const float* g = gamma_tile + head * 128;
+      const float* cr = p.rope_cos + row * half;
+      const float* sr = p.rope_sin + row * half;
+      const int split = (half / 2) & ~7;
+      const int pr0 = part == 0 ? 0 : split, pr1 = part == 0 ? split : half;
+      int i = pr0;
+      if ((half & 3) == 0) {  // 8 pairs at a time with 16-byte table loads (rows stay 16-byte aligned)
+        for (; i + 8 <= pr1; i += 8) {
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr + i), c1 = *reinterpret_cast<const f32x4*>(cr + i + 4);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr + i), s1 = *reinterpret_cast<const f32x4*>(sr + i + 4);
+          const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = f32_to_bf16_rne(t[q * 8 + 2 * e]) | (f32_to_bf16_rne(t[q * 8 + 2 * e + 1]) << 16);
-          *reinterpret_cast<u32x4*>(orow + q * 8) = o;
+          for (int e = 0; e < 8; ++e) {
+            const float a = t[i + e] * inv * g[i + e], b = t[i + e + half] * inv * g[i + e + half];
+            t[i + e] = a * cs[e] - b * sn[e];
+            t[i + e + half] = b * cs[e] + a * sn[e];
+          }
         }
+      }
+      for (; i < pr1; ++i) {
+        const float a = t[i] * inv * g[i], b = t[i + half] * inv * g[i + half];
+        const float c = cr[i], s = sr[i];
+        t[i] = a * c - b * s;
+        t[i + half] = b * c + a * s;
+      }
+      const int rest = 128 - 2 * half;
+      const int q0 = 2 * half + (part == 0 ? 0 : rest / 2), q1 = part == 0 ? 2 * half + rest / 2 : 128;
+      for (int k = q0; k < q1; ++k) t[k] = t[k] * inv * g[k];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (row < p.S) {  // the head's 16 chunks of 8: part 0 stores the first 8, part 1 the rest
+      uint16_t* orow = p.out + row * p.out_ld + static_cast<int64_t>(nt) * BN + head * 128;
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        const int q = part * 8 + qq;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = f32_to_bf16_rne(t[q * 8 + 2 * e]) | (f32_to_bf16_rne(t[q * 8 + 2 * e + 1]) << 16);
+        *reinterpret_cast<u32x4*>(orow + q * 8) = o;
       }
     }
   }

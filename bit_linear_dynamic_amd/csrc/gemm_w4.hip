@@ -301,6 +301,41 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
+// Plain output through LDS: the tile goes into the freed stages as bf16 [128][264] (8 padding
+// columns per row keep the two row groups of one 2-byte store on different banks), then every
+// thread stores 16 chunks of 8 consecutive output columns with 16-byte stores. Needs the output
+// rows 16-byte aligned (n_out a multiple of 8, or of 16 for a gate/up weight, and out aligned).
+constexpr int kOutPitch = 264;
+static_assert(BM * kOutPitch * 2 <= kLdsBytes, "output staging must fit the stages");
+
+__device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const f32x16 (&acc)[4][2],
+                                                      uint8_t* smem, float scale, int64_t m0, int nt, int wave,
+                                                      uint32_t lane) {
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
+        const int col = wave * 64 + j * 32 + static_cast<int>(lane & 31);
+        tile[row * kOutPitch + col] = static_cast<uint16_t>(f32_to_bf16_hw(scale * acc[i][j][r]));
+      }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < BM * BN / 8 / kThreads; ++q) {
+    const int c = static_cast<int>(threadIdx.x) + kThreads * q;
+    const int row = c >> 5, c8 = (c & 31) * 8;
+    const int64_t grow = m0 + row;
+    const int64_t n = packed_row_source(nt, c8, p.gate_up != 0, p.n_out);
+    if (grow < p.S && n >= 0)
+      *reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n) =
+          *reinterpret_cast<const u32x4*>(tile + row * kOutPitch + c8);
+  }
+}
+
 // Q/K tiles of the fused QKV projection (MiniMax-H3 Ultra Fast, "Active optimization stack",
 // attention projections, and "Kernel path" item 2; 96 of 128 head dimensions rotate: MiniMax-H3
 // Turbo CMF card, "On parity"). The tile's 256 columns are two heads of 128. Per row and head:
@@ -394,7 +429,7 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          o[e] = f32_to_bf16_rne(t[q * 8 + 2 * e]) | (f32_to_bf16_rne(t[q * 8 + 2 * e + 1]) << 16);
+          o[e] = f32_to_bf16_hw(t[q * 8 + 2 * e]) | (f32_to_bf16_hw(t[q * 8 + 2 * e + 1]) << 16);
         *reinterpret_cast<u32x4*>(orow + q * 8) = o;
       }
     }
@@ -583,6 +618,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
       return;
     }
   }
+  if constexpr (EPI != 1) {
+    const bool rows16 = (p.out_ld & 7) == 0 && (p.n_out & (p.gate_up ? 15 : 7)) == 0 &&
+                        (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+    if (rows16) {
+      plain_epilogue_staged(p, acc, smem, scale, m0, nt, wave, lane);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -595,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
         for (int j = 0; j < 2; ++j) {
           const int cl = static_cast<int>(ncol[j]);
           const int64_t n = p.gate_up ? packed_row_source(nt, cl, true, p.n_out) : static_cast<int64_t>(nt) * BN + cl;
-          if (n >= 0 && n < p.n_out) orow[n] = static_cast<uint16_t>(f32_to_bf16_rne(scale * acc[i][j][r]));
+          if (n >= 0 && n < p.n_out) orow[n] = static_cast<uint16_t>(f32_to_bf16_hw(scale * acc[i][j][r]));
         }
       } else {
         // this wave's 64 tile columns are 32 gate columns then the 32 matching up columns
@@ -603,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
         if (n < p.n_out) {
           const float g = scale * acc[i][0][r];
           const float u = scale * acc[i][1][r];
-          orow[n] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * u));
+          orow[n] = static_cast<uint16_t>(f32_to_bf16_hw(silu(g) * u));
         }
       }
     }

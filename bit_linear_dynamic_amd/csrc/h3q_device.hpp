@@ -31,6 +31,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// fp32 -> bf16 bits by the hardware conversion (v_cvt_pk_bf16_f32: round to nearest even).
+__device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
 // E4M3 ("FN": bias 7, no inf, NaN = 0x7F) scale in byte SEL of w -> fp32. gfx950's
 // v_cvt_f32_fp8 decodes the OCP E4M3FN variant (checked over all 256 codes against the format table).
 template <int SEL>

@@ -132,6 +132,7 @@ CASES = [
     (300, 1024, 520, 128, 128.0, 1.0, False),
     (513, 320, 256, 512, 64.0, 0.5, False),
     (100, 512, 2 * 200, 128, 128.0, 1.0, True),
+    (70, 96, 2 * 116, 16, 8.0, 1.0, True),       # F not a multiple of 8: the 2-byte store path
 ]
 
 
@@ -156,6 +157,29 @@ def test_parity_with_oracle(S, K, N, rank, alpha, strength, gate_up):
                 herr = normwise(h, oracle.swiglu(ref))
                 say(f"  swiglu normwise={herr:.3e}")
                 assert herr <= TOL
+    finally:
+        p.free()
+
+
+@pytest.mark.parametrize("N,gate_up", [(520, False), (2 * 200, True)])
+def test_store_paths_agree(N, gate_up):
+    """Outputs whose rows are 16-byte aligned go through the LDS-staged 16-byte stores; the same call
+    into a buffer offset by one element takes the 2-byte store path. Both must agree bit for bit."""
+    S, K = 261, 320
+    say(f"store paths N={N} gate_up={gate_up}")
+    p = Proj(N, K, 950 + N, gate_up=gate_up)
+    try:
+        p.add_adapter(1, 32, 16.0, 951, 952)
+        x, pqs = dev(synth.activation(S, K, 953)), dev(synth.pre_quant_scale(K, 954))
+        flags = (0,) + ((h3q.H3Q_EPI_SWIGLU,) if gate_up else ())
+        for fl in flags:
+            n_out = N // 2 if fl else N
+            aligned = h3q.h3q_linear_ex(x, pqs, p.handle, 1, 1.0, fl)
+            buf = torch.full((S * n_out + 1,), -1.0, dtype=torch.bfloat16, device="cuda")
+            shifted = h3q.h3q_linear_ex(x, pqs, p.handle, 1, 1.0, fl, out=buf[1:].view(S, n_out))
+            torch.cuda.synchronize()
+            assert buf[0].item() == -1.0, "store before the output"
+            assert torch.equal(aligned, shifted), fl
     finally:
         p.free()
 

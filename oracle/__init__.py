@@ -9,7 +9,9 @@ Method (FL2VA Turbo page, section "Implementation"):
     y = NVFP4_base(x * pre_quant_scale) + strength * (alpha / rank) * B(A x)
 with the LoRA branch on the original bf16 activation. W4A4 variant: the base path's activation is
 itself quantized to NVFP4 per call (MiniMax-H3 Ultra Fast, "Kernel path"). Gate/up output feeds
-SiLU(gate) * up (same page, "Active optimization stack", MLP row).
+SiLU(gate) * up (same page, "Active optimization stack", MLP row). For comparison only, the merged
+route (the LoRA update merged into the weight before quantizing: MiniMax-H3 Turbo CMF card, "What the
+conversion did") is ``merge_lora`` + ``quantize_nvfp4``.
 
 Every function here is pinned by tests/test_oracle_*.py against things other than itself: the
 format's published code tables and torch's float8 conversion, exact rational arithmetic on small
@@ -61,6 +63,8 @@ def _declare(lib):
     lib.orc_swiglu.argtypes, lib.orc_swiglu.restype = [vp, i64, i64, vp], None
     lib.orc_qk_norm_rope.argtypes = [vp, i64, i64, i64, i32, f64, vp, vp, vp, vp, vp]
     lib.orc_qk_norm_rope.restype = None
+    lib.orc_merge_lora.argtypes = [vp, vp, f32, i64, i64, vp, vp, i64, f64, f64, vp, vp]
+    lib.orc_merge_lora.restype = i32
     lib.orc_num_threads.argtypes, lib.orc_num_threads.restype = [], i32
     return lib
 
@@ -184,6 +188,28 @@ def qk_norm_rope(y: np.ndarray, q_width: int, rot_dim: int, eps: float, gamma_q,
     (lib or load()).orc_qk_norm_rope(_ptr(y), M, N, int(q_width), int(rot_dim), float(eps),
                                      _ptr(gamma_q), _ptr(gamma_k), _ptr(cos), _ptr(sin), _ptr(out))
     return out
+
+
+def merge_lora(codes, scales, ts, A_bits=None, B_bits=None, rank=0, alpha=0.0, strength=0.0, pqs=None,
+               lib=None) -> np.ndarray:
+    """fp32 [N][K] merged weight m = f32(Wd + c * (B A) / pqs) (see oracle.cpp, orc_merge_lora); feed it
+    to quantize_nvfp4 for the merged NVFP4 weight."""
+    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    m = np.empty((N, K), np.float32)
+    A_bits, B_bits, pqs = _c(A_bits, np.uint16), _c(B_bits, np.uint16), _c(pqs, np.float32)
+    rc = (lib or load()).orc_merge_lora(_ptr(codes), _ptr(scales), float(ts), N, K, _ptr(A_bits), _ptr(B_bits),
+                                        int(rank), float(alpha), float(strength), _ptr(pqs), _ptr(m))
+    if rc != 0:
+        raise ValueError("orc_merge_lora: bad shape")
+    return m
+
+
+def merged_nvfp4(codes, scales, ts, A_bits=None, B_bits=None, rank=0, alpha=0.0, strength=0.0, pqs=None,
+                 lib=None):
+    """The merged route end to end: (codes, scales, ts) of NVFP4(merge_lora(...))."""
+    return quantize_nvfp4(merge_lora(codes, scales, ts, A_bits, B_bits, rank, alpha, strength, pqs, lib=lib),
+                          lib=lib)
 
 
 def num_threads(lib=None) -> int:

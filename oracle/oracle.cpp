@@ -277,6 +277,36 @@ void orc_qk_norm_rope(const double* y, int64_t M, int64_t N, int64_t qw, int32_t
   }
 }
 
+// Merged route, for comparison with the dynamic path (the LoRA update merged into the weight before
+// quantizing: MiniMax-H3 Turbo CMF card, "What the conversion did", backbone item, and "Which file";
+// the dynamic path of FL2VA Turbo, "Implementation", never does this). The base weight acts on
+// x (*) pqs, so a merged weight that reproduces base + c B (A x) carries the adapter term divided by
+// pqs per input column:
+//   m[n][k] = f32( Wd[n][k] + (c * sum_j B[n][j] * A[j][k]) / pqs[k] ),   c = strength * alpha / rank
+// in fp64 with j ascending and one rounding to fp32 at the end; pqs NULL means ones. Then
+// m (x (*) pqs) = Wd (x (*) pqs) + c B (A x) up to that rounding. Quantizing m with
+// orc_quantize_nvfp4 gives the merged NVFP4 weight. codes/scales: [N][K/2] / [N][K/16]; A: bf16
+// [rank][K]; B: bf16 [N][rank]; m: fp32 [N][K]. rank == 0 or A == NULL merges nothing.
+int orc_merge_lora(const uint8_t* codes, const uint8_t* scales, float ts, int64_t N, int64_t K,
+                   const uint16_t* A, const uint16_t* B, int64_t rank, double alpha, double strength,
+                   const float* pqs, float* m) {
+  if (K % 16 != 0 || N < 0 || rank < 0) return -1;
+  std::vector<double> Wd(static_cast<size_t>(N * K));
+  orc_dequant(codes, scales, static_cast<double>(ts), N, K, Wd.data());
+  const bool lora = (A != nullptr && B != nullptr && rank > 0);
+  const double c = lora ? strength * alpha / static_cast<double>(rank) : 0.0;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      double s = 0.0;
+      for (int64_t j = 0; lora && j < rank; ++j)
+        s += bf16_to_double(B[n * rank + j]) * bf16_to_double(A[j * K + k]);
+      const double p = pqs ? static_cast<double>(pqs[k]) : 1.0;
+      m[n * K + k] = static_cast<float>(Wd[n * K + k] + c * s / p);
+    }
+  return 0;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

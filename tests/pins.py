@@ -461,4 +461,36 @@ def pin_rope_complex_rotation(lib):
         assert np.array_equal(got[:, 2 * qw:], y[:, 2 * qw:])
 
 
+def pin_merge_reproduces_dynamic_linear(lib):
+    """The merged fp32 weight applied to x (*) pqs reproduces the dynamic linear (itself pinned to
+    numpy and exact fractions) up to m's one fp32 rounding, for pqs != 1, alpha != rank, negative
+    strength and N != K; and with no adapter m is Wd rounded to fp32."""
+    rng = np.random.default_rng(33)
+    for (M, K, N, r, alpha, strength) in [(6, 48, 7, 3, 1.5, 0.7), (5, 64, 33, 16, 16.0, 1.0), (4, 32, 6, 2, 8.0, -1.5)]:
+        x, pqs, codes, scales, ts, A, B = _lora_case(rng, M, K, N, r, lib)
+        m = oracle.merge_lora(codes, scales, ts, A, B, r, alpha, strength, pqs, lib=lib)
+        assert m.dtype == np.float32 and m.shape == (N, K)
+        xs = bf16_values(x) * pqs.astype(np.float64)
+        got = xs @ m.astype(np.float64).T
+        want = oracle.linear(x, pqs, codes, scales, ts, A, B, r, alpha, strength, lib=lib)
+        err = np.abs(got - want).max() / np.abs(want).max()
+        assert err < 1e-6, err
+        m0 = oracle.merge_lora(codes, scales, ts, pqs=pqs, lib=lib)
+        assert np.array_equal(m0, decode_independent(codes, scales, ts).astype(np.float32))
+
+
+def pin_merge_rank1_exact(lib):
+    """Rank 1 with dyadic a, b and power-of-two pqs: every fp64 step is exact, so
+    m[n][k] = f32(Wd[n][k] + c a_k b_n / pqs_k) with c = strength alpha / rank, element for element."""
+    rng = np.random.default_rng(34)
+    N, K = 5, 32
+    codes, scales, ts = random_nvfp4(N, K, rng, lib=lib)
+    a = rng.integers(-4, 5, K) / 8.0
+    b = rng.integers(-4, 5, N) / 8.0
+    pqs = (2.0 ** rng.integers(-2, 3, K)).astype(np.float32)
+    m = oracle.merge_lora(codes, scales, ts, bits_of(a[None, :]), bits_of(b[:, None]), 1, 2.0, 0.75, pqs, lib=lib)
+    want = decode_independent(codes, scales, ts) + 1.5 * np.outer(b, a) / pqs.astype(np.float64)
+    assert np.array_equal(m, want.astype(np.float32))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -56,6 +56,14 @@ MUTANTS = [
     ("rmsnorm_eps_outside", "1.0 / std::sqrt(ss / static_cast<double>(hd) + eps)",
      "1.0 / (std::sqrt(ss / static_cast<double>(hd)) + eps)", 0),
     ("rmsnorm_gamma_swapped", "c0 < qw ? gamma_q + c0 : gamma_k + (c0 - qw)", "c0 < qw ? gamma_k + c0 : gamma_q + (c0 - qw)", 0),
+    ("merge_pqs_multiplied", "m[n * K + k] = static_cast<float>(Wd[n * K + k] + c * s / p);",
+     "m[n * K + k] = static_cast<float>(Wd[n * K + k] + c * s * p);", 0),
+    ("merge_c_dropped", "m[n * K + k] = static_cast<float>(Wd[n * K + k] + c * s / p);",
+     "m[n * K + k] = static_cast<float>(Wd[n * K + k] + s / p);", 0),
+    ("merge_A_transposed", "s += bf16_to_double(B[n * rank + j]) * bf16_to_double(A[j * K + k]);",
+     "s += bf16_to_double(B[n * rank + j]) * bf16_to_double(A[k * rank + j]);", 0),
+    ("merge_base_dropped", "m[n * K + k] = static_cast<float>(Wd[n * K + k] + c * s / p);",
+     "m[n * K + k] = static_cast<float>(c * s / p);", 0),
     ("rmsnorm_touches_v", "for (int64_t c0 = 0; c0 < 2 * qw; c0 += hd) {", "for (int64_t c0 = 0; c0 < N; c0 += hd) {", 0),
 ]
 

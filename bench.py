@@ -131,6 +131,55 @@ def cpu_baseline(projs, S, rows_per_proj):
             "seconds": dt}
 
 
+def merged_vs_dynamic(projs, stream, calls=5):
+    """Per projection: the dynamic call (LoRA-down + GEMM over K + r_pad) against a base-only call on
+    the weight with the update merged in before quantizing (h3q_merge_adapter, then packed), both with
+    pqs; plus what one merge costs (device merge + quantize, synchronous) and the host-side pack. The
+    accuracy side of the comparison (the merged route re-rounds the adapted weight to NVFP4) is
+    measured against the oracle by the tests, not here."""
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+
+    def per_call_ms(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(calls):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / calls
+
+    out, tot = {}, {"dynamic_ms": 0.0, "merged_ms": 0.0}
+    for d in projs:
+        p = d["p"]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        codes, scales, ts = h3q.h3q_merge_adapter(d["handle"], 1, 1.0, d["pqs"])
+        merge_ms = (time.perf_counter() - t0) * 1e3
+        t0 = time.perf_counter()
+        mh = h3q.h3q_pack_weight(codes.cpu(), scales.cpu(), ts.item(), p.N, p.K,
+                                 h3q.H3Q_PACK_GATE_UP if p.gate_up else 0)
+        pack_ms = (time.perf_counter() - t0) * 1e3
+        del codes, scales
+        try:
+            dyn = per_call_ms(lambda: h3q.h3q_linear(d["x"], d["pqs"], d["handle"], 1, 1.0, y=d["y"], stream=stream))
+            mrg = per_call_ms(lambda: h3q.h3q_linear(d["x"], d["pqs"], mh, h3q.H3Q_ADAPTER_NONE, 0.0, y=d["y"],
+                                                     stream=stream))
+        finally:
+            h3q.h3q_free_weight(mh)
+        out[p.name] = {"dynamic_ms": round(dyn, 4), "merged_ms": round(mrg, 4),
+                       "dynamic_overhead_pct": round(100.0 * (dyn - mrg) / mrg, 2),
+                       "merge_ms": round(merge_ms, 2), "pack_host_ms": round(pack_ms, 1)}
+        tot["dynamic_ms"] += dyn
+        tot["merged_ms"] += mrg
+    out["block"] = {"dynamic_ms": round(tot["dynamic_ms"], 4), "merged_ms": round(tot["merged_ms"], 4),
+                    "dynamic_overhead_pct": round(100.0 * (tot["dynamic_ms"] - tot["merged_ms"]) / tot["merged_ms"], 2)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -219,6 +268,9 @@ def main():
         qk = {"gemm_ms": round(gq / gqn, 4), "plain_gemm_ms": plain,
               "epilogue_overhead_pct": round(100.0 * (gq / gqn - plain) / plain, 2)}
 
+    # the merged route (the update folded into the weight before quantizing) against the dynamic call
+    mvd = merged_vs_dynamic(projs, stream)
+
     cpu = None
     if not args.no_cpu:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
@@ -251,6 +303,7 @@ def main():
         "kernels_ms_per_step": {"gemm": round(gemm_ms / args.steps, 4), "lora_down": round(down_ms / args.steps, 4)},
         "per_projection": per_proj,
         "qkv_with_qk_norm_rope": qk,
+        "merged_vs_dynamic": mvd,
         "cpu_baseline": cpu,
     }
     for d in projs:

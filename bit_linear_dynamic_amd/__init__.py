@@ -51,6 +51,7 @@ def _declare(lib):
         "h3q_linear_qk_norm_rope": [vp, vp, i64, vp, vp, i32, f32, u32, i64, i32, f32, vp, vp, vp, vp, vp],
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_dequant": [vp, vp, vp],
+        "h3q_merge_adapter": [vp, vp, i32, f32, vp, vp, vp, vp, vp],
         "h3q_weight_checksum": [vp, vp, ctypes.POINTER(ctypes.c_uint64)],
         "h3q_timing_enable": [i32],
         "h3q_timing_get": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
@@ -224,6 +225,24 @@ def h3q_linear_qk_norm_rope(x, pqs, w: int, adapter_id: int, strength: float, q_
         _dev_ptr(rope_cos, torch.float32, "rope_cos"), _dev_ptr(rope_sin, torch.float32, "rope_sin"),
         _dev_ptr(y, torch.bfloat16, "y")))
     return y
+
+
+def h3q_merge_adapter(w: int, adapter_id: int, strength: float, pqs=None, merged: bool = False, stream=None):
+    """The merged route (for comparison): NVFP4 of Wq*ts + c*(B A)/pqs. Returns device tensors
+    (codes u8 [N][K/2], scales u8 [N][K/16], ts fp32 [1]) and, if merged, the fp32 [N][K] m."""
+    import torch
+    N, K, _ = h3q_weight_info(w)
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if pqs is not None and tuple(pqs.shape) != (K,):
+        raise ValueError(f"pqs must be [{K}]")
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty((1,), dtype=torch.float32, device=dev)
+    m = torch.empty((N, K), dtype=torch.float32, device=dev) if merged else None
+    _check(lib().h3q_merge_adapter(_stream(stream), ctypes.c_void_p(w), int(adapter_id), float(strength),
+                                   _dev_ptr(pqs, torch.float32, "pqs"), _dev_ptr(codes), _dev_ptr(scales),
+                                   _dev_ptr(ts), _dev_ptr(m, torch.float32, "merged")))
+    return (codes, scales, ts, m) if merged else (codes, scales, ts)
 
 
 def h3q_quantize_nvfp4(x, pqs=None, stream=None):

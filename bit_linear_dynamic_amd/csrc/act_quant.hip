@@ -14,7 +14,8 @@
 //   * code: no division at all -- |v| is compared in fp64 with the seven E2M1 decision points
 //     (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) * d, d = E4M3(s_b) * ts, all exact products; on a tie
 //     the comparison direction picks the neighbour with the even mantissa bit.
-// Two passes: a grid-wide amax (atomic max on the fp32 bit pattern, exact and order-free), then one
+// The same quantizer serves the merged-weight route on an fp32 input (ActQuantParams::xf: v = the
+// input itself). Two passes: a grid-wide amax (atomic max on the fp32 bit pattern, exact and order-free), then one
 // thread per 16-element block. The second pass can also write the decoded activation
 // E2M1 * E4M3 (exact bf16, tensor scale left to the GEMM epilogue) as the GEMM's operand.
 #include "h3q_device.hpp"
@@ -34,12 +35,20 @@ __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 __global__ __launch_bounds__(256) void amax_kernel(ActQuantParams p) {
   const int64_t total = p.S * p.K;
   float m = 0.0f;
-  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 2; i < total;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x * 2) {
-    const uint32_t two = *reinterpret_cast<const uint32_t*>(p.x + i);  // K even: pairs stay in a row
-    const int64_t k = i % p.K;
-    m = fmaxf(m, fabsf(prescaled(two & 0xffffu, p.pqs, k)));
-    m = fmaxf(m, fabsf(prescaled(two >> 16, p.pqs, k + 1)));
+  if (p.xf) {  // fp32 input (K % 16 == 0, so quads never cross a row)
+    for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < total;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x * 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.xf + i);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+  } else {
+    for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 2; i < total;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x * 2) {
+      const uint32_t two = *reinterpret_cast<const uint32_t*>(p.x + i);  // K even: pairs stay in a row
+      const int64_t k = i % p.K;
+      m = fmaxf(m, fabsf(prescaled(two & 0xffffu, p.pqs, k)));
+      m = fmaxf(m, fabsf(prescaled(two >> 16, p.pqs, k + 1)));
+    }
   }
   // wave64 reduction, then one atomic per wave (|v| >= 0: fp32 bit patterns order as unsigned)
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -82,17 +91,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActQuantParams p) {
        idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t row = idx / blocks_per_row;
     const int64_t k0 = (idx - row * blocks_per_row) * 16;
-    const u32x4 x0 = *reinterpret_cast<const u32x4*>(p.x + row * p.K + k0);
-    const u32x4 x1 = *reinterpret_cast<const u32x4*>(p.x + row * p.K + k0 + 8);
-    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     float v[16];
+    if (p.xf) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 f = *reinterpret_cast<const f32x4*>(p.xf + row * p.K + k0 + 4 * q);
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+    } else {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(p.x + row * p.K + k0);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(p.x + row * p.K + k0 + 8);
+      const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = prescaled(xw[i] & 0xffffu, p.pqs, k0 + 2 * i);
+        v[2 * i + 1] = prescaled(xw[i] >> 16, p.pqs, k0 + 2 * i + 1);
+      }
+    }
     float amax_b = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = prescaled(xw[i] & 0xffffu, p.pqs, k0 + 2 * i);
-      v[2 * i + 1] = prescaled(xw[i] >> 16, p.pqs, k0 + 2 * i + 1);
-      amax_b = fmaxf(amax_b, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
-    }
+    for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
     const uint32_t sc = e4m3_rne_satfinite(static_cast<double>(amax_b) / six_ts);
     const float s = e4m3_byte_to_f32<0>(sc);
     const double d = static_cast<double>(s) * static_cast<double>(ts);  // exact

@@ -580,6 +580,52 @@ h3q_status h3q_debug_dequant(void* stream, h3q_weight w, uint16_t* wq) {
   return ok();
 }
 
+h3q_status h3q_merge_adapter(void* stream_, h3q_weight w, int32_t adapter_id, float strength, const float* pqs,
+                             uint8_t* codes, uint8_t* scales, float* ts, float* merged) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!live(w)) return fail(H3Q_E_ARG, "merge_adapter: not a live weight handle");
+  if (!codes || !scales || !ts) return fail(H3Q_E_ARG, "merge_adapter: null output");
+  if ((reinterpret_cast<uintptr_t>(codes) & 7u) || (merged && !aligned16(merged)) || (pqs && !aligned16(pqs)))
+    return fail(H3Q_E_ARG, "merge_adapter: codes must be 8-byte, pqs and merged 16-byte aligned");
+  if (!std::isfinite(strength)) return fail(H3Q_E_ARG, "merge_adapter: strength must be finite");
+  int dev;
+  if (h3q_status st = check_device(&dev)) return st;
+  if (dev != w->device) return fail(H3Q_E_ARG, "merge_adapter: weight lives on device %d, current is %d", w->device, dev);
+  Adapter ad;
+  if (adapter_id != H3Q_ADAPTER_NONE) {
+    std::lock_guard<std::mutex> lk(w->mu);
+    auto it = w->adapters.find(adapter_id);
+    if (it == w->adapters.end()) return fail(H3Q_E_ADAPTER, "merge_adapter: unknown adapter id %d", adapter_id);
+    ad = it->second;  // device buffers stay owned by the handle
+  }
+  const bool lora = ad.rank > 0 && strength != 0.0f;
+  const int64_t N = w->N, K = w->K;
+  const size_t wq_bytes = static_cast<size_t>(N * K * 2);
+  const size_t m_bytes = merged ? 0 : static_cast<size_t>(N * K * 4);
+  void* tmp = nullptr;
+  if (dev_alloc(&tmp, 256 + wq_bytes + m_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(H3Q_E_NOMEM, "merge_adapter: temporary allocation of %zu bytes failed", 256 + wq_bytes + m_bytes);
+  }
+  uint8_t* t8 = static_cast<uint8_t*>(tmp);
+  uint16_t* wq = reinterpret_cast<uint16_t*>(t8 + 256);
+  float* m = merged ? merged : reinterpret_cast<float*>(t8 + 256 + wq_bytes);
+  DequantParams dq{reinterpret_cast<const uint32_t*>(w->codes), reinterpret_cast<const uint32_t*>(w->scales),
+                   w->n_tiles, w->k_tiles, gate_up(w), N, K, wq};
+  MergeParams mp{wq, ad.A, ad.B, pqs, m, static_cast<double>(w->ts),
+                 lora ? static_cast<double>(strength) * ad.alpha / static_cast<double>(ad.rank) : 0.0,
+                 N, K, w->K_pad, w->n_tiles, lora ? ad.r_pad : 0, gate_up(w)};
+  ActQuantParams q{nullptr, nullptr, N, K, reinterpret_cast<uint32_t*>(t8), ts, codes, scales, nullptr, K, m};
+  hipError_t e = launch_debug_dequant(dq, stream);
+  if (e == hipSuccess) e = launch_lora_merge(mp, stream);
+  if (e == hipSuccess) e = launch_act_quant(q, stream);
+  const hipError_t es = hipStreamSynchronize(stream);  // the temporaries are freed below
+  (void)hipFree(tmp);
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "merge_adapter launch: %s", hipGetErrorString(e));
+  if (es != hipSuccess) return fail(H3Q_E_HIP, "merge_adapter: %s", hipGetErrorString(es));
+  return ok();
+}
+
 h3q_status h3q_weight_checksum(void* stream, h3q_weight w, uint64_t* out) {
   if (!live(w)) return fail(H3Q_E_ARG, "weight_checksum: not a live weight handle");
   if (!out) return fail(H3Q_E_ARG, "weight_checksum: null output");

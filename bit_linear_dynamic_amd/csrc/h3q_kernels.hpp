@@ -87,6 +87,7 @@ struct ActQuantParams {
   uint8_t* scales;          // [S][K/16] or null
   uint16_t* xq_out;         // bf16 [S][xq_ld] = E2M1 * E4M3 (no ts), or null
   int64_t xq_ld;            // >= K; columns [K, xq_ld) are written as zero
+  const float* xf = nullptr; // fp32 [S][K] input used as v instead of x * pqs (x, pqs unused), or null
 };
 hipError_t launch_act_quant(const ActQuantParams& p, hipStream_t stream);
 
@@ -114,5 +115,19 @@ struct DequantParams {
   uint16_t* out;            // bf16 [N][K]
 };
 hipError_t launch_debug_dequant(const DequantParams& p, hipStream_t stream);
+
+// Merged route (merge.hip): m = f32(Wq * ts + c * (B A) / pqs) in fp64, rows in the caller's order.
+struct MergeParams {
+  const uint16_t* wq;       // bf16 [N][K] = E2M1 * E4M3 (from the dequant kernel)
+  const uint16_t* A;        // adapter A, bf16 [r_pad][K_pad] (unused when r_pad == 0)
+  const uint16_t* B;        // adapter B, bf16 [n_tiles][r_pad/32][256][32]
+  const float* pqs;         // [K] or null (ones)
+  float* m;                 // fp32 [N][K]
+  double ts, c;             // weight tensor scale; strength * alpha / rank (0 without an adapter)
+  int64_t N, K, K_pad;
+  int32_t n_tiles, r_pad;
+  bool gate_up;
+};
+hipError_t launch_lora_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace h3q

@@ -137,6 +137,26 @@ h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, c
                                    int32_t rot_dim, float eps, const float* gamma_q, const float* gamma_k,
                                    const float* rope_cos, const float* rope_sin, uint16_t* y);
 
+/* The merged route, for comparison with the dynamic path only: the adapter's update folded into the
+ * weight before quantizing, as a converter that bakes a LoRA into a 4-bit checkpoint does (MiniMax-H3
+ * Turbo CMF card, "What the conversion did", backbone item; "Which file"), where the dynamic path
+ * keeps base and adapter apart on every call (FL2VA Turbo, "Implementation"). With Wq the packed
+ * weight's E2M1 * E4M3 values, ts its tensor scale and c = strength * alpha / rank:
+ *   m[n][k] = f32( Wq[n][k] * ts + (c * sum_j B[n][j] * A[j][k]) / pqs[k] )   fp64, j ascending
+ * (pqs NULL -> ones; the division keeps m (x * pqs) = base + c B (A x) up to m's fp32 rounding), then
+ * m is quantized exactly as h3q_quantize_nvfp4 quantizes v. adapter_id H3Q_ADAPTER_NONE, or strength
+ * 0, merges nothing (a plain re-quantization of the decoded weight). Outputs, device pointers in the
+ * caller's row order (gate/up weights: rows [0, N/2) gate, [N/2, N) up), ready for h3q_pack_weight
+ * after a copy to the host:
+ *   codes uint8 [N][K/2] (8-byte aligned), scales uint8 [N][K/16], ts fp32 [1],
+ *   merged fp32 [N][K] (16-byte aligned) or NULL -- the unquantized m, if wanted.
+ * pqs: device fp32 [K] (16-byte aligned) or NULL. Allocates N * K * 2 (+ N * K * 4 when merged is
+ * NULL) bytes of temporary device memory and synchronizes `stream` before returning. The handle and
+ * its adapter are not modified. Errors: unknown adapter -> H3Q_E_ADAPTER; null or misaligned output,
+ * non-finite strength -> H3Q_E_ARG; allocation -> H3Q_E_NOMEM. */
+h3q_status h3q_merge_adapter(void* stream, h3q_weight w, int32_t adapter_id, float strength, const float* pqs,
+                             uint8_t* codes, uint8_t* scales, float* ts, float* merged);
+
 /* The W4A4 activation quantizer on its own (MiniMax-H3 Ultra Fast, "Kernel path", item 1), as
  * h3q_linear_ex(H3Q_ACT_NVFP4) runs it:
  *   v      = f32(x) * pqs[k] rounded to fp32            (pqs NULL -> v = x)

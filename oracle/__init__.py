@@ -11,7 +11,9 @@ with the LoRA branch on the original bf16 activation. W4A4 variant: the base pat
 itself quantized to NVFP4 per call (MiniMax-H3 Ultra Fast, "Kernel path"). Gate/up output feeds
 SiLU(gate) * up (same page, "Active optimization stack", MLP row). For comparison only, the merged
 route (the LoRA update merged into the weight before quantizing: MiniMax-H3 Turbo CMF card, "What the
-conversion did") is ``merge_lora`` + ``quantize_nvfp4``.
+conversion did") is ``merge_lora`` + ``quantize_nvfp4``. The AdaLN modulation curve of the same card
+(the adapter folded into a rank-24 table by the same K-concatenation) is ``adaln_table`` +
+``adaln_apply``.
 
 Every function here is pinned by tests/test_oracle_*.py against things other than itself: the
 format's published code tables and torch's float8 conversion, exact rational arithmetic on small
@@ -65,6 +67,10 @@ def _declare(lib):
     lib.orc_qk_norm_rope.restype = None
     lib.orc_merge_lora.argtypes = [vp, vp, f32, i64, i64, vp, vp, i64, f64, f64, vp, vp]
     lib.orc_merge_lora.restype = i32
+    lib.orc_adaln_table.argtypes = [vp, vp, vp, f64, i64, i64, i64, i64, i64, vp]
+    lib.orc_adaln_table.restype = None
+    lib.orc_adaln_apply.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.orc_adaln_apply.restype = None
     lib.orc_num_threads.argtypes, lib.orc_num_threads.restype = [], i32
     return lib
 
@@ -210,6 +216,34 @@ def merged_nvfp4(codes, scales, ts, A_bits=None, B_bits=None, rank=0, alpha=0.0,
     """The merged route end to end: (codes, scales, ts) of NVFP4(merge_lora(...))."""
     return quantize_nvfp4(merge_lora(codes, scales, ts, A_bits, B_bits, rank, alpha, strength, pqs, lib=lib),
                           lib=lib)
+
+
+def adaln_table(u, emb, A_bits, c, lib=None) -> np.ndarray:
+    """fp64 [blocks][S][rb + rl] = [u ; c * A_b silu(e)] per sample (see oracle.cpp, orc_adaln_table).
+    u: [S][rb]; emb: [S][E]; A_bits: bf16 bits [blocks][rl][E]."""
+    u, emb, A_bits = _c(u, np.float32), _c(emb, np.float32), _c(A_bits, np.uint16)
+    S, rb = u.shape
+    blocks, rl, E = A_bits.shape
+    if emb.shape != (S, E):
+        raise ValueError("adaln_table: emb must be [S][E]")
+    out = np.empty((blocks, S, rb + rl), np.float64)
+    (lib or load()).orc_adaln_table(_ptr(u), _ptr(emb), _ptr(A_bits), float(c), blocks, S, E, rb, rl, _ptr(out))
+    return out
+
+
+def adaln_apply(M_bits, bias, table, t, lib=None) -> np.ndarray:
+    """fp64 [T][blocks][rows] = bias + M v(t), v interpolated from the table (orc_adaln_apply).
+    M_bits: bf16 bits [blocks][rows][R]; bias: [blocks][rows] or None; table: [blocks][S][R]; t: [T]."""
+    M_bits, bias = _c(M_bits, np.uint16), _c(bias, np.float32)
+    table, t = _c(table, np.float64), _c(np.atleast_1d(t), np.float32)
+    blocks, rows, R = M_bits.shape
+    S = table.shape[1]
+    if table.shape != (blocks, S, R) or S < 2:
+        raise ValueError("adaln_apply: table must be [blocks][S >= 2][R]")
+    out = np.empty((t.shape[0], blocks, rows), np.float64)
+    (lib or load()).orc_adaln_apply(_ptr(M_bits), _ptr(bias), _ptr(table), _ptr(t), t.shape[0], blocks, rows, S, R,
+                                    _ptr(out))
+    return out
 
 
 def num_threads(lib=None) -> int:

@@ -307,6 +307,64 @@ int orc_merge_lora(const uint8_t* codes, const uint8_t* scales, float ts, int64_
   return 0;
 }
 
+// AdaLN modulation as a rank-24 curve (MiniMax-H3 Turbo CMF card, "What the conversion did";
+// MiniMax-H3 Ultra Fast, "Why the pruned transformer matters"). Per block b the modulation vector is
+//   adaln_b(t) = W_p,b u(t) + bias_b + c B_b (A_b silu(e(t)))  =  [W_p,b | B_b] v_b(t) + bias_b,
+//   v_b(t) = [u(t) ; c A_b silu(e(t))],
+// with u the pruned checkpoint's rb-value time coordinate (shared by every block), A_b [rl][E] and B_b
+// the adapter's factors written against the full modulation matrix, e(t) the E-wide timestep
+// embedding and c = strength * alpha / rank. u and e are sampled at S points of t in [0, 1]
+// (t_i = i / (S - 1)); v_b is tabulated at those points and linearly interpolated between them.
+//
+// orc_adaln_table: table[b][i][q] = u[i][q] for q < rb, c * sum_k A_b[q - rb][k] * silu(emb[i][k])
+//   otherwise (silu(z) = z / (1 + exp(-z)), fp64). u: fp32 [S][rb]; emb: fp32 [S][E]; A: bf16
+//   [blocks][rl][E]; table: fp64 [blocks][S][rb + rl].
+void orc_adaln_table(const float* u, const float* emb, const uint16_t* A, double c, int64_t blocks, int64_t S,
+                     int64_t E, int64_t rb, int64_t rl, double* table) {
+  const int64_t R = rb + rl;
+  for (int64_t b = 0; b < blocks; ++b)
+    for (int64_t i = 0; i < S; ++i) {
+      double* row = table + (b * S + i) * R;
+      for (int64_t q = 0; q < rb; ++q) row[q] = static_cast<double>(u[i * rb + q]);
+      for (int64_t j = 0; j < rl; ++j) {
+        double s = 0.0;
+        for (int64_t k = 0; k < E; ++k) {
+          const double z = static_cast<double>(emb[i * E + k]);
+          s += bf16_to_double(A[(b * rl + j) * E + k]) * (z / (1.0 + std::exp(-z)));
+        }
+        row[rb + j] = c * s;
+      }
+    }
+}
+
+// orc_adaln_apply: for each requested t (clamped to [0, 1]): p = t (S - 1), i0 = min(floor(p), S - 2),
+//   th = p - i0, v = (1 - th) table[b][i0] + th table[b][i0 + 1], and
+//   out[tau][b][r] = bias[b][r] + sum_q M[b][r][q] v[q]   (fp64).
+// M: bf16 [blocks][rows][R] = [W_p | B] row by row; bias: fp32 [blocks][rows] or NULL; table: fp64
+// [blocks][S][R]; t: fp32 [T]; out: fp64 [T][blocks][rows]. Needs S >= 2.
+void orc_adaln_apply(const uint16_t* M, const float* bias, const double* table, const float* t, int64_t T,
+                     int64_t blocks, int64_t rows, int64_t S, int64_t R, double* out) {
+  std::vector<double> v(static_cast<size_t>(R));
+  for (int64_t tau = 0; tau < T; ++tau) {
+    double tt = static_cast<double>(t[tau]);
+    tt = tt < 0.0 ? 0.0 : (tt > 1.0 ? 1.0 : tt);
+    const double p = tt * static_cast<double>(S - 1);
+    int64_t i0 = static_cast<int64_t>(std::floor(p));
+    if (i0 > S - 2) i0 = S - 2;
+    const double th = p - static_cast<double>(i0);
+    for (int64_t b = 0; b < blocks; ++b) {
+      const double* t0 = table + (b * S + i0) * R;
+      const double* t1 = t0 + R;
+      for (int64_t q = 0; q < R; ++q) v[q] = (1.0 - th) * t0[q] + th * t1[q];
+      for (int64_t r = 0; r < rows; ++r) {
+        double acc = bias ? static_cast<double>(bias[b * rows + r]) : 0.0;
+        for (int64_t q = 0; q < R; ++q) acc += bf16_to_double(M[(b * rows + r) * R + q]) * v[q];
+        out[(tau * blocks + b) * rows + r] = acc;
+      }
+    }
+  }
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

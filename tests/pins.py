@@ -493,4 +493,70 @@ def pin_merge_rank1_exact(lib):
     assert np.array_equal(m, want.astype(np.float32))
 
 
+def _adaln_case(rng, blocks=2, S=5, E=12, rb=3, rl=2, rows=7):
+    u = rng.standard_normal((S, rb)).astype(np.float32)
+    emb = rng.uniform(-4, 4, (S, E)).astype(np.float32)
+    A = random_bf16((blocks, rl, E), 0.5, rng)
+    Wp = random_bf16((blocks, rows, rb), 0.5, rng)
+    B = random_bf16((blocks, rows, rl), 0.5, rng)
+    bias = rng.standard_normal((blocks, rows)).astype(np.float32)
+    return u, emb, A, Wp, B, bias
+
+
+def pin_adaln_fold_identity(lib):
+    """The folded form [W_p | B] [u ; c A silu(e)] + bias, evaluated through the table at the sample
+    points, equals the unfolded W_p u + bias + c B (A silu(e)) computed with numpy, block by block."""
+    rng = np.random.default_rng(35)
+    u, emb, A, Wp, B, bias = _adaln_case(rng)
+    blocks, rows, rb = Wp.shape
+    S, c = u.shape[0], -0.75
+    table = oracle.adaln_table(u, emb, A, c, lib=lib)
+    M = np.concatenate([Wp, B], axis=2)
+    ts = (np.arange(S) / (S - 1)).astype(np.float32)
+    got = oracle.adaln_apply(M, bias, table, ts, lib=lib)
+    e = emb.astype(np.float64)
+    silu = e / (1.0 + np.exp(-e))
+    for b in range(blocks):
+        Av, Wv, Bv = bf16_values(A[b]), bf16_values(Wp[b]), bf16_values(B[b])
+        want = (Wv @ u.astype(np.float64).T + bias[b].astype(np.float64)[:, None] + c * Bv @ (Av @ silu.T)).T
+        np.testing.assert_allclose(got[:, b, :], want, rtol=1e-12, atol=1e-12)
+    # no adapter term: the rank-8 base curve alone
+    t0 = oracle.adaln_table(u, emb, A, 0.0, lib=lib)
+    got0 = oracle.adaln_apply(M, None, t0, ts, lib=lib)
+    np.testing.assert_allclose(got0[:, 0, :], (bf16_values(Wp[0]) @ u.astype(np.float64).T).T, rtol=1e-13, atol=1e-13)
+
+
+def pin_adaln_silu_points(lib):
+    """silu at points with closed forms: silu(0) = 0 and silu(ln 3) = 0.75 ln 3 (sigmoid(ln 3) = 3/4),
+    through a one-hot A row."""
+    E = 4
+    emb = np.array([[0.0, 0.0, 0.0, 0.0], [np.log(3.0)] * 4], np.float32)
+    u = np.zeros((2, 1), np.float32)
+    A = bits_of(np.array([[[1.0, 0.0, 0.0, 0.0]]]))
+    table = oracle.adaln_table(u, emb, A, 2.0, lib=lib)
+    z = float(np.float32(np.log(3.0)))
+    assert table[0, 0, 1] == 0.0
+    np.testing.assert_allclose(table[0, 1, 1], 2.0 * z / (1.0 + np.exp(-z)), rtol=1e-15)
+    np.testing.assert_allclose(table[0, 1, 1], 2.0 * 0.75 * np.log(3.0), rtol=1e-7)
+    assert table.shape == (1, 2, 2) and E == 4
+
+
+def pin_adaln_interpolation(lib):
+    """Between samples the curve is the affine blend of its neighbours; t = 0 and t = 1 give the first
+    and last samples exactly; t outside [0, 1] is clamped."""
+    rng = np.random.default_rng(36)
+    blocks, S, R, rows = 2, 9, 4, 5
+    table = rng.standard_normal((blocks, S, R))
+    M = random_bf16((blocks, rows, R), 1.0, rng)
+    at = lambda t: oracle.adaln_apply(M, None, table, np.array([t], np.float32), lib=lib)[0]
+    exact = lambda i: np.einsum("brq,bq->br", bf16_values(M), table[:, i, :])
+    np.testing.assert_allclose(at(0.0), exact(0), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(at(1.0), exact(S - 1), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(at(-0.5), exact(0), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(at(2.0), exact(S - 1), rtol=1e-14, atol=1e-14)
+    for i, th in ((2, 0.25), (5, 0.5), (7, 0.75)):
+        t = (i + th) / (S - 1)   # exact in fp32 for S - 1 = 8
+        np.testing.assert_allclose(at(t), (1 - th) * exact(i) + th * exact(i + 1), rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

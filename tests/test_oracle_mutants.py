@@ -64,6 +64,14 @@ MUTANTS = [
      "s += bf16_to_double(B[n * rank + j]) * bf16_to_double(A[k * rank + j]);", 0),
     ("merge_base_dropped", "m[n * K + k] = static_cast<float>(Wd[n * K + k] + c * s / p);",
      "m[n * K + k] = static_cast<float>(c * s / p);", 0),
+    ("adaln_table_order", "for (int64_t q = 0; q < rb; ++q) row[q] = static_cast<double>(u[i * rb + q]);",
+     "for (int64_t q = 0; q < rb; ++q) row[rl + q] = static_cast<double>(u[i * rb + q]);", 0),
+    ("adaln_silu_dropped", "s += bf16_to_double(A[(b * rl + j) * E + k]) * (z / (1.0 + std::exp(-z)));",
+     "s += bf16_to_double(A[(b * rl + j) * E + k]) * z;", 0),
+    ("adaln_c_dropped", "row[rb + j] = c * s;", "row[rb + j] = s;", 0),
+    ("adaln_interp_swapped", "v[q] = (1.0 - th) * t0[q] + th * t1[q];", "v[q] = th * t0[q] + (1.0 - th) * t1[q];", 0),
+    ("adaln_grid_S", "const double p = tt * static_cast<double>(S - 1);", "const double p = tt * static_cast<double>(S);", 0),
+    ("adaln_bias_dropped", "double acc = bias ? static_cast<double>(bias[b * rows + r]) : 0.0;", "double acc = 0.0;", 0),
     ("rmsnorm_touches_v", "for (int64_t c0 = 0; c0 < 2 * qw; c0 += hd) {", "for (int64_t c0 = 0; c0 < N; c0 += hd) {", 0),
 ]
 

@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--proj", choices=["qkv", "attn_out", "gate_up", "down"], default=None,
                     help="profiling aid: time one projection only (the JSON line then covers only it)")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="profiling aid: skip the per-projection, Q/K-epilogue and merged-vs-dynamic passes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="profiling aid: run only a plain device copy of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -180,6 +182,45 @@ def merged_vs_dynamic(projs, stream, calls=5):
     return out
 
 
+def adaln_curve(stream, device, reps=50):
+    """The AdaLN modulation curve of all 50 blocks ([96768, 24] each, 1025 samples, rank 8 + 16) at
+    T = 2 times per call: apply time and its HBM rate (bytes = blocks * rows * (2 R + 4 + 4 T)), and
+    the one-off table build."""
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+    from bit_linear_dynamic_amd import synth
+    from bit_linear_dynamic_amd import workloads as wl
+
+    c = wl.ADALN
+    u, emb, A, M, bias = synth.adaln_curve_inputs(c.blocks, c.samples, c.emb_dim, c.base_rank, c.lora_rank, c.rows,
+                                                  synth.seed_of(9, 0, 0), device)
+    u, emb = u.to(device), emb.to(device)
+    t = torch.tensor([0.8125, 0.30078125], dtype=torch.float32, device=device)
+    table = h3q.h3q_adaln_table(u, emb, A, 1.0, stream=stream)
+    out = h3q.h3q_adaln_apply(M, bias, table, t, stream=stream)
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    build_ms = timed(lambda: h3q.h3q_adaln_table(u, emb, A, 1.0, stream=stream))
+    apply_ms = timed(lambda: h3q.h3q_adaln_apply(M, bias, table, t, out=out, stream=stream))
+    R, T = c.base_rank + c.lora_rank, t.shape[0]
+    bytes_apply = c.blocks * c.rows * (2 * R + 4 + 4 * T)
+    gbs = bytes_apply / (apply_ms * 1e-3) / 1e9
+    return {"blocks": c.blocks, "rows": c.rows, "R": R, "samples": c.samples, "T": T,
+            "apply_us": round(apply_ms * 1e3, 2), "apply_bytes": bytes_apply, "apply_GBps": round(gbs, 1),
+            "apply_hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "table_build_us": round(build_ms * 1e3, 2),
+            "table_flop": 2 * c.blocks * c.samples * c.lora_rank * c.emb_dim}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -233,7 +274,7 @@ def main():
 
     # per-projection breakdown (separate, untimed-above pass with timing on)
     per_proj = {}
-    for d in projs:
+    for d in ([] if args.timed_only else projs):
         h3q.h3q_timing_enable(True)
         for _ in range(3):
             h3q.h3q_linear(d["x"], d["pqs"], d["handle"], 1, 1.0, y=d["y"])
@@ -249,7 +290,7 @@ def main():
     qk = None
     for d in projs:
         p = d["p"]
-        if p.name != "qkv":
+        if p.name != "qkv" or args.timed_only:
             continue
         from bit_linear_dynamic_amd import synth
         q_width = p.N // 3
@@ -269,7 +310,8 @@ def main():
               "epilogue_overhead_pct": round(100.0 * (gq / gqn - plain) / plain, 2)}
 
     # the merged route (the update folded into the weight before quantizing) against the dynamic call
-    mvd = merged_vs_dynamic(projs, stream)
+    mvd = None if args.timed_only else merged_vs_dynamic(projs, stream)
+    adaln = None if args.timed_only else adaln_curve(stream, device)
 
     cpu = None
     if not args.no_cpu:
@@ -304,6 +346,7 @@ def main():
         "per_projection": per_proj,
         "qkv_with_qk_norm_rope": qk,
         "merged_vs_dynamic": mvd,
+        "adaln_curve": adaln,
         "cpu_baseline": cpu,
     }
     for d in projs:

@@ -52,6 +52,8 @@ def _declare(lib):
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_dequant": [vp, vp, vp],
         "h3q_merge_adapter": [vp, vp, i32, f32, vp, vp, vp, vp, vp],
+        "h3q_adaln_table": [vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, vp],
+        "h3q_adaln_apply": [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp],
         "h3q_weight_checksum": [vp, vp, ctypes.POINTER(ctypes.c_uint64)],
         "h3q_timing_enable": [i32],
         "h3q_timing_get": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
@@ -243,6 +245,43 @@ def h3q_merge_adapter(w: int, adapter_id: int, strength: float, pqs=None, merged
                                    _dev_ptr(pqs, torch.float32, "pqs"), _dev_ptr(codes), _dev_ptr(scales),
                                    _dev_ptr(ts), _dev_ptr(m, torch.float32, "merged")))
     return (codes, scales, ts, m) if merged else (codes, scales, ts)
+
+
+def h3q_adaln_table(u, emb, A, scale: float, stream=None):
+    """Device u fp32 [S][rb], emb fp32 [S][E], A bf16 [blocks][rl][E] (or None) -> fp32 table
+    [blocks][S][rb + rl] = [u ; scale * A_b silu(emb)]."""
+    import torch
+    S, rb = u.shape
+    E = emb.shape[1]
+    if tuple(emb.shape) != (S, E):
+        raise ValueError("emb must be [S][E]")
+    blocks, rl = (A.shape[0], A.shape[1]) if A is not None else (1, 0)
+    if A is not None and A.shape[2] != E:
+        raise ValueError("A must be [blocks][rl][E]")
+    table = torch.empty((blocks, S, rb + rl), dtype=torch.float32, device=u.device)
+    _check(lib().h3q_adaln_table(_stream(stream), _dev_ptr(u, torch.float32, "u"), _dev_ptr(emb, torch.float32, "emb"),
+                                 _dev_ptr(A, torch.bfloat16, "A"), float(scale), blocks, S, E, rb, rl,
+                                 _dev_ptr(table, torch.float32, "table")))
+    return table
+
+
+def h3q_adaln_apply(M, bias, table, t, out=None, stream=None):
+    """Device M bf16 [blocks][rows][R], bias fp32 [blocks][rows] or None, table fp32 [blocks][S][R],
+    t fp32 [T] -> out fp32 [T][blocks][rows] = bias + M v(t)."""
+    import torch
+    blocks, rows, R = M.shape
+    S = table.shape[1]
+    if tuple(table.shape) != (blocks, S, R):
+        raise ValueError("table must be [blocks][S][R]")
+    T = t.shape[0]
+    if out is None:
+        out = torch.empty((T, blocks, rows), dtype=torch.float32, device=M.device)
+    elif tuple(out.shape) != (T, blocks, rows):
+        raise ValueError(f"out must be [{T}][{blocks}][{rows}]")
+    _check(lib().h3q_adaln_apply(_stream(stream), _dev_ptr(M, torch.bfloat16, "M"), _dev_ptr(bias, torch.float32, "bias"),
+                                 _dev_ptr(table, torch.float32, "table"), _dev_ptr(t, torch.float32, "t"), T, blocks,
+                                 rows, S, R, _dev_ptr(out, torch.float32, "out")))
+    return out
 
 
 def h3q_quantize_nvfp4(x, pqs=None, stream=None):

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3q.so")
 
-SOURCES = ["h3q_api.cpp", "gemm_w4.hip", "lora_down.hip", "act_quant.hip", "misc.hip", "merge.hip"]
+SOURCES = ["h3q_api.cpp", "gemm_w4.hip", "lora_down.hip", "act_quant.hip", "misc.hip", "merge.hip", "adaln.hip"]
 # The GEMM-shaped kernels are scheduled for instruction-level parallelism rather than register
 # pressure: they run one wave per SIMD anyway, and this lets LDS operand reads run ahead of the MFMAs.
 PER_FILE = {"gemm_w4.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],

@@ -331,8 +331,8 @@ __device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const
     const int64_t grow = m0 + row;
     const int64_t n = packed_row_source(nt, c8, p.gate_up != 0, p.n_out);
     if (grow < p.S && n >= 0)
-      *reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n) =
-          *reinterpret_cast<const u32x4*>(tile + row * kOutPitch + c8);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile + row * kOutPitch + c8),
+                                  reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n));
   }
 }
 

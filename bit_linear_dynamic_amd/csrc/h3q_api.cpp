@@ -626,6 +626,38 @@ h3q_status h3q_merge_adapter(void* stream_, h3q_weight w, int32_t adapter_id, fl
   return ok();
 }
 
+h3q_status h3q_adaln_table(void* stream, const float* u, const float* emb, const uint16_t* A, float scale,
+                           int32_t blocks, int32_t samples, int32_t emb_dim, int32_t base_rank, int32_t lora_rank,
+                           float* table) {
+  if (!u || !emb || !table || (lora_rank > 0 && !A)) return fail(H3Q_E_ARG, "adaln_table: null pointer");
+  if (blocks < 1 || blocks > 65535 || samples < 2 || emb_dim < 1 || base_rank < 1 || base_rank > 64 || lora_rank < 0 || lora_rank > 32 ||
+      base_rank + lora_rank > 64 || static_cast<int64_t>(samples) * emb_dim > (int64_t{1} << 31))
+    return fail(H3Q_E_SHAPE, "adaln_table: need blocks >= 1, samples >= 2, emb_dim >= 1, 1 <= base_rank, 0 <= lora_rank <= 32, "
+                "base_rank + lora_rank <= 64");
+  if (!std::isfinite(scale)) return fail(H3Q_E_ARG, "adaln_table: scale must be finite");
+  int dev;
+  if (h3q_status st = check_device(&dev)) return st;
+  AdalnTableParams p{u, emb, A, scale, blocks, samples, emb_dim, base_rank, lora_rank, table};
+  hipError_t e = launch_adaln_table(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "adaln_table launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+h3q_status h3q_adaln_apply(void* stream, const uint16_t* M, const float* bias, const float* table, const float* t,
+                           int32_t T, int32_t blocks, int64_t rows, int32_t samples, int32_t R, float* out) {
+  if (!M || !table || !t || !out) return fail(H3Q_E_ARG, "adaln_apply: null pointer");
+  if (T < 1 || T > 8 || blocks < 1 || blocks > 65535 || rows < 0 || rows > (int64_t{1} << 24) || samples < 2 || R < 8 || R > 64 || R % 8 != 0)
+    return fail(H3Q_E_SHAPE, "adaln_apply: need 1 <= T <= 8, blocks >= 1, 0 <= rows <= 2^24, samples >= 2, "
+                "R a multiple of 8 in [8, 64]");
+  if (!aligned16(M)) return fail(H3Q_E_ARG, "adaln_apply: M must be 16-byte aligned");
+  int dev;
+  if (h3q_status st = check_device(&dev)) return st;
+  AdalnApplyParams p{M, bias, table, t, T, blocks, samples, R, rows, out};
+  hipError_t e = launch_adaln_apply(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "adaln_apply launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 h3q_status h3q_weight_checksum(void* stream, h3q_weight w, uint64_t* out) {
   if (!live(w)) return fail(H3Q_E_ARG, "weight_checksum: not a live weight handle");
   if (!out) return fail(H3Q_E_ARG, "weight_checksum: null output");

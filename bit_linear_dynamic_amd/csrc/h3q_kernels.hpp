@@ -130,4 +130,26 @@ struct MergeParams {
 };
 hipError_t launch_lora_merge(const MergeParams& p, hipStream_t stream);
 
+// AdaLN modulation curve (adaln.hip).
+struct AdalnTableParams {
+  const float* u;           // fp32 [S][rb], shared by the blocks
+  const float* emb;         // fp32 [S][E]
+  const uint16_t* A;        // bf16 [blocks][rl][E] (unused when rl == 0)
+  float c;                  // strength * alpha / rank
+  int32_t blocks, S, E, rb, rl;  // rl <= 32
+  float* table;             // fp32 [blocks][S][rb + rl]
+};
+hipError_t launch_adaln_table(const AdalnTableParams& p, hipStream_t stream);
+
+struct AdalnApplyParams {
+  const uint16_t* M;        // bf16 [blocks][rows][R], 16-byte aligned, R % 8 == 0, R <= 64
+  const float* bias;        // fp32 [blocks][rows] or null
+  const float* table;       // fp32 [blocks][S][R]
+  const float* t;           // fp32 [T], T <= 8
+  int32_t T, blocks, S, R;
+  int64_t rows;
+  float* out;               // fp32 [T][blocks][rows]
+};
+hipError_t launch_adaln_apply(const AdalnApplyParams& p, hipStream_t stream);
+
 }  // namespace h3q

@@ -7,7 +7,8 @@ workloads name:
     pqs ~ U[0.5, 2]    as fp32   (per-input-channel pre_quant_scale)
     W   ~ N(0, 0.02)   as fp32   (weight before NVFP4 quantization)
     A,B ~ N(0, 0.01)   as bf16   (LoRA factors)
-where N(0, s) names the standard deviation s. Draws use torch's seeded generators on the device
+and, for the AdaLN modulation curve, smooth time coordinates and sinusoidal timestep features
+(adaln_curve_inputs), where N(0, s) names the standard deviation s. Draws use torch's seeded generators on the device
 the tensor is made on; the same tensor is then handed to both sides of a comparison, so no two
 implementations of a generator ever need to agree.
 """
@@ -95,3 +96,32 @@ def rope_table(S: int, rot_dim: int, frame_hw=(48, 84), base: float = 10000.0, d
         cols.append(pos[:, a:a + 1] * freq[None, :])
     theta = torch.cat(cols, dim=1) if cols else torch.zeros((S, 0), dtype=torch.float64)
     return theta.cos().float().to(device), theta.sin().float().to(device)
+
+
+def adaln_curve_inputs(blocks: int, samples: int, emb_dim: int, base_rank: int, lora_rank: int, rows: int,
+                       seed: int, device="cpu"):
+    """Synthetic inputs of the AdaLN modulation curve, at the sample points t_i = i / (samples - 1):
+      u    fp32 [samples][base_rank]: the time coordinate, u_q(t) = a_q cos((q + 1) pi t + phi_q) with
+           amplitudes a_q = 0.3^q * N(1, 0.1) (a smooth curve whose components decay like the
+           singular values the pages list);
+      emb  fp32 [samples][emb_dim]: sinusoidal features of 1000 t (half cosines, half sines, periods
+           spread geometrically up to 10000), a stand-in for the model's timestep embedding;
+      A    bf16 [blocks][lora_rank][emb_dim] ~ N(0, 0.01);
+      M    bf16 [blocks][rows][base_rank + lora_rank] = [W_p ~ N(0, 0.1) | B ~ N(0, 0.01)];
+      bias fp32 [blocks][rows] ~ N(0, 0.1)."""
+    t = torch.linspace(0.0, 1.0, samples, dtype=torch.float64)
+    amp = (0.3 ** torch.arange(base_rank, dtype=torch.float64)) * (1.0 + 0.1 * normal((base_rank,), 1.0, seed).double())
+    phase = uniform((base_rank,), 0.0, 6.283185307179586, seed + 1).double()
+    q = torch.arange(base_rank, dtype=torch.float64)
+    u = amp[None, :] * torch.cos((q[None, :] + 1.0) * torch.pi * t[:, None] + phase[None, :])
+    half = emb_dim // 2
+    freq = 10000.0 ** (-torch.arange(half, dtype=torch.float64) / max(half, 1))
+    arg = 1000.0 * t[:, None] * freq[None, :]
+    emb = torch.cat([torch.cos(arg), torch.sin(arg)], dim=1)
+    if emb.shape[1] < emb_dim:
+        emb = torch.cat([emb, torch.zeros((samples, emb_dim - emb.shape[1]), dtype=torch.float64)], dim=1)
+    A = normal((blocks, lora_rank, emb_dim), 0.01, seed + 2, device, torch.bfloat16)
+    Wp = normal((blocks, rows, base_rank), 0.1, seed + 3, device, torch.bfloat16)
+    B = normal((blocks, rows, lora_rank), 0.01, seed + 4, device, torch.bfloat16)
+    bias = normal((blocks, rows), 0.1, seed + 5, device)
+    return (u.float().to(device), emb.float().to(device), A, torch.cat([Wp, B], dim=2).contiguous(), bias)

@@ -50,3 +50,21 @@ def effective_flops(S: int, p: Projection, with_adapter: bool = True) -> int:
     if with_adapter:
         f += 2 * S * p.rank * (p.K + p.N)
     return f
+
+
+@dataclass(frozen=True)
+class AdalnCurve:
+    """The AdaLN modulation curve of the pruned model with the adapter folded in (MiniMax-H3 Turbo CMF
+    card, "What the conversion did": [1025, 8] time table shared by the blocks, [96768, 8] per-block
+    weights, lora_A [16, 2688], a [1025, 24] table per block; 50 denoiser blocks: FL2VA Turbo,
+    "Implementation")."""
+    blocks: int = 50
+    samples: int = 1025
+    emb_dim: int = 2688
+    base_rank: int = 8
+    lora_rank: int = 16
+    rows: int = 96768
+
+
+ADALN = AdalnCurve()
+ADALN_SMALL = AdalnCurve(blocks=3, samples=33, emb_dim=200, base_rank=8, lora_rank=16, rows=1000)

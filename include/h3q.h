@@ -157,6 +157,35 @@ h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, c
 h3q_status h3q_merge_adapter(void* stream, h3q_weight w, int32_t adapter_id, float strength, const float* pqs,
                              uint8_t* codes, uint8_t* scales, float* ts, float* merged);
 
+/* The AdaLN modulation curve with the adapter folded in by the same K-concatenation as the main GEMM
+ * (MiniMax-H3 Turbo CMF card, "What the conversion did": the pruned modulation W_p u(t) plus the
+ * adapter's B (A silu(e(t))) become one rank-24 curve [W_p | B] [u(t) ; A silu(e(t))] driven by a
+ * per-block table; MiniMax-H3 Ultra Fast, "Why the pruned transformer matters": u is an 8-value
+ * coordinate sampled at 1025 points and interpolated linearly, the modulation matrix is [96768, 8]).
+ *
+ * h3q_adaln_table: table[b][i] = [ u[i][0..rb) ; scale * A_b silu(emb[i]) ] for the `samples` points
+ * t_i = i / (samples - 1), fp32 accumulation, silu(z) = z / (1 + exp(-z)); scale = strength * alpha /
+ * rank of the adapter (rebuild the table to change either). Device pointers:
+ *   u      fp32 [samples][base_rank]        (shared by every block)
+ *   emb    fp32 [samples][emb_dim]          (the timestep embedding at the sample points)
+ *   A      bf16 [blocks][lora_rank][emb_dim] (NULL if lora_rank is 0)
+ *   table  fp32 [blocks][samples][base_rank + lora_rank]
+ * 1 <= blocks <= 65535, samples >= 2, 1 <= base_rank, 0 <= lora_rank <= 32, base_rank + lora_rank <= 64.
+ * Asynchronous.
+ *
+ * h3q_adaln_apply: for each of the T requested times (clamped to [0, 1]), with p = t (samples - 1),
+ * i0 = min(floor(p), samples - 2), th = p - i0 and v = (1 - th) table[b][i0] + th table[b][i0 + 1]:
+ *   out[tau][b][r] = bias[b][r] + sum_q M[b][r][q] v[q]          (fp32)
+ *   M      bf16 [blocks][rows][R], row r = [W_p row | B row], 16-byte aligned; R % 8 == 0, 8 <= R <= 64
+ *   bias   fp32 [blocks][rows] or NULL;  table  fp32 [blocks][samples][R];  t  fp32 [T], 1 <= T <= 8
+ *   out    fp32 [T][blocks][rows]
+ * Asynchronous on `stream`. */
+h3q_status h3q_adaln_table(void* stream, const float* u, const float* emb, const uint16_t* A, float scale,
+                           int32_t blocks, int32_t samples, int32_t emb_dim, int32_t base_rank, int32_t lora_rank,
+                           float* table);
+h3q_status h3q_adaln_apply(void* stream, const uint16_t* M, const float* bias, const float* table, const float* t,
+                           int32_t T, int32_t blocks, int64_t rows, int32_t samples, int32_t R, float* out);
+
 /* The W4A4 activation quantizer on its own (MiniMax-H3 Ultra Fast, "Kernel path", item 1), as
  * h3q_linear_ex(H3Q_ACT_NVFP4) runs it:
  *   v      = f32(x) * pqs[k] rounded to fp32            (pqs NULL -> v = x)

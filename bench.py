@@ -182,6 +182,53 @@ def merged_vs_dynamic(projs, stream, calls=5):
     return out
 
 
+def producer_fusion(projs, stream, calls=5):
+    """The MLP pair gate/up -> down per call, unfused (SwiGLU writes h; the down call makes its own
+    base operand bf16(h * pqs) in LoRA-down or the prescale pass) against fused (the SwiGLU epilogue
+    also writes that operand; the down call takes it as given), with adapter 1 at strength 1 and with
+    no adapter."""
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+
+    by = {d["p"].name: d for d in projs}
+    if "gate_up" not in by or "down" not in by:
+        return None
+    gu, dn = by["gate_up"], by["down"]
+    S, F = gu["x"].shape[0], gu["p"].N // 2
+    h = torch.empty((S, F), dtype=torch.bfloat16, device=gu["x"].device)
+    xs = torch.empty_like(h)
+
+    def unfused(aid, st):
+        h3q.h3q_linear_swiglu(gu["x"], gu["pqs"], gu["handle"], aid, st, h=h, stream=stream)
+        h3q.h3q_linear(h, dn["pqs"], dn["handle"], aid, st, y=dn["y"], stream=stream)
+
+    def fused(aid, st):
+        h3q.h3q_linear_swiglu_emit(gu["x"], gu["pqs"], gu["handle"], aid, st, dn["pqs"], h=h, xs_next=xs,
+                                   stream=stream)
+        h3q.h3q_linear_prescaled(h, xs, dn["handle"], aid, st, y=dn["y"], stream=stream)
+
+    def per_call_ms(fn, aid, st):
+        fn(aid, st)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(calls):
+            fn(aid, st)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / calls
+
+    out = {}
+    for name, aid, st in (("adapter", 1, 1.0), ("no_adapter", h3q.H3Q_ADAPTER_NONE, 0.0)):
+        # alternate the two orders so that neither always runs on a warmer or cooler chip
+        u1, f1 = per_call_ms(unfused, aid, st), per_call_ms(fused, aid, st)
+        f2, u2 = per_call_ms(fused, aid, st), per_call_ms(unfused, aid, st)
+        u, f = (u1 + u2) / 2, (f1 + f2) / 2
+        out[name] = {"unfused_ms": round(u, 4), "fused_ms": round(f, 4), "fused_vs_unfused_pct": round(100 * (f - u) / u, 2)}
+    return out
+
+
 def adaln_curve(stream, device, reps=50):
     """The AdaLN modulation curve of all 50 blocks ([96768, 24] each, 1025 samples, rank 8 + 16) at
     T = 2 times per call: apply time and its HBM rate (bytes = blocks * rows * (2 R + 4 + 4 T)), and
@@ -312,6 +359,7 @@ def main():
     # the merged route (the update folded into the weight before quantizing) against the dynamic call
     mvd = None if args.timed_only else merged_vs_dynamic(projs, stream)
     adaln = None if args.timed_only else adaln_curve(stream, device)
+    fusion = None if args.timed_only else producer_fusion(projs, stream)
 
     cpu = None
     if not args.no_cpu:
@@ -347,6 +395,7 @@ def main():
         "qkv_with_qk_norm_rope": qk,
         "merged_vs_dynamic": mvd,
         "adaln_curve": adaln,
+        "mlp_producer_fusion": fusion,
         "cpu_baseline": cpu,
     }
     for d in projs:

@@ -52,6 +52,8 @@ def _declare(lib):
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_dequant": [vp, vp, vp],
         "h3q_merge_adapter": [vp, vp, i32, f32, vp, vp, vp, vp, vp],
+        "h3q_linear_swiglu_emit": [vp, vp, i64, vp, vp, i32, f32, u32, vp, vp, vp],
+        "h3q_linear_prescaled": [vp, vp, vp, i64, vp, i32, f32, vp],
         "h3q_adaln_table": [vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, vp],
         "h3q_adaln_apply": [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp],
         "h3q_weight_checksum": [vp, vp, ctypes.POINTER(ctypes.c_uint64)],
@@ -195,6 +197,45 @@ def h3q_linear(x, pqs, w: int, adapter_id: int, strength: float, y=None, stream=
 
 def h3q_linear_swiglu(x, pqs, w: int, adapter_id: int, strength: float, h=None, stream=None):
     return h3q_linear_ex(x, pqs, w, adapter_id, strength, H3Q_EPI_SWIGLU, h, stream)
+
+
+def h3q_linear_swiglu_emit(x, pqs, w: int, adapter_id: int, strength: float, pqs_next, flags: int = 0, h=None,
+                           xs_next=None, stream=None):
+    """SwiGLU projection that also emits the next projection's base operand bf16(h * pqs_next).
+    Returns (h, xs_next), both device bf16 [S][N/2]."""
+    import torch
+    N, K, _ = h3q_weight_info(w)
+    S, F = x.shape[0], N // 2
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [S][{K}]")
+    if tuple(pqs_next.shape) != (F,):
+        raise ValueError(f"pqs_next must be [{F}]")
+    h = torch.empty((S, F), dtype=torch.bfloat16, device=x.device) if h is None else h
+    xs_next = torch.empty((S, F), dtype=torch.bfloat16, device=x.device) if xs_next is None else xs_next
+    if tuple(h.shape) != (S, F) or tuple(xs_next.shape) != (S, F):
+        raise ValueError(f"h and xs_next must be [{S}][{F}]")
+    _check(lib().h3q_linear_swiglu_emit(_stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S,
+                                        _dev_ptr(pqs, torch.float32, "pqs"), ctypes.c_void_p(w), int(adapter_id),
+                                        float(strength), int(flags), _dev_ptr(h, torch.bfloat16, "h"),
+                                        _dev_ptr(pqs_next, torch.float32, "pqs_next"),
+                                        _dev_ptr(xs_next, torch.bfloat16, "xs_next")))
+    return h, xs_next
+
+
+def h3q_linear_prescaled(x, xs, w: int, adapter_id: int, strength: float, y=None, stream=None):
+    """h3q_linear with the base operand xs (= bf16(x * pqs)) given; x feeds the LoRA branch only."""
+    import torch
+    N, K, _ = h3q_weight_info(w)
+    S = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K or tuple(xs.shape) != (S, K):
+        raise ValueError(f"x and xs must be [S][{K}]")
+    y = torch.empty((S, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    if tuple(y.shape) != (S, N):
+        raise ValueError(f"y must be [{S}][{N}]")
+    _check(lib().h3q_linear_prescaled(_stream(stream), _dev_ptr(x, torch.bfloat16, "x"),
+                                      _dev_ptr(xs, torch.bfloat16, "xs"), S, ctypes.c_void_p(w), int(adapter_id),
+                                      float(strength), _dev_ptr(y, torch.bfloat16, "y")))
+    return y
 
 
 def h3q_linear_qk_norm_rope(x, pqs, w: int, adapter_id: int, strength: float, q_width: int, rot_dim: int,

@@ -336,6 +336,57 @@ __device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const
   }
 }
 
+// SwiGLU output through LDS: h = bf16(SiLU(gate) * up) as a bf16 [128][136] tile in the freed stages
+// (wave w holds h columns [32w, 32w + 32)), then 16-byte stores of 8 consecutive h columns. With an
+// emit target the same pass also writes the next projection's base operand
+// xs = bf16(f32(h) * pqs_next[n]) from the stored h bits, i.e. exactly what prescaling the stored h
+// would give (FL2VA Turbo, "Implementation": the producer emitting the base input beside the exact bf16
+// LoRA input). Needs n_out % 8 == 0 and 16-byte aligned rows.
+constexpr int kHPitch = 136;
+static_assert(BM * kHPitch * 2 <= kLdsBytes, "SwiGLU staging must fit the stages");
+
+__device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, const f32x16 (&acc)[4][2],
+                                                       uint8_t* smem, float scale, int64_t m0, int nt, int wave,
+                                                       uint32_t lane) {
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = i * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
+      const int col = wave * 32 + static_cast<int>(lane & 31);
+      const float g = scale * acc[i][0][r];
+      const float u = scale * acc[i][1][r];
+      tile[row * kHPitch + col] = static_cast<uint16_t>(f32_to_bf16_hw(silu(g) * u));
+      if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // 4 values at a time: accumulators stay in AGPRs
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < BM * (BN / 2) / 8 / kThreads; ++q) {
+    const int c = static_cast<int>(threadIdx.x) + kThreads * q;
+    const int row = c >> 4, c8 = (c & 15) * 8;
+    const int64_t grow = m0 + row;
+    const int64_t n = static_cast<int64_t>(nt) * (BN / 2) + c8;
+    if (grow >= p.S || n >= p.n_out) continue;
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(tile + row * kHPitch + c8);
+    __builtin_nontemporal_store(hv, reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n));
+    if (p.emit_out) {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(p.emit_pqs + n);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(p.emit_pqs + n + 4);
+      const float pq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+      uint32_t xw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xw[e] = f32_to_bf16_hw(bf16_bits_to_f32(hw[e] & 0xffffu) * pq[2 * e]) |
+                (f32_to_bf16_hw(bf16_bits_to_f32(hw[e] >> 16) * pq[2 * e + 1]) << 16);
+      __builtin_nontemporal_store(u32x4{xw[0], xw[1], xw[2], xw[3]},
+                                  reinterpret_cast<u32x4*>(p.emit_out + grow * p.emit_ld + n));
+    }
+  }
+}
+
 // Q/K tiles of the fused QKV projection (MiniMax-H3 Ultra Fast, "Active optimization stack",
 // attention projections, and "Kernel path" item 2; 96 of 128 head dimensions rotate: MiniMax-H3
 // Turbo CMF card, "On parity"). The tile's 256 columns are two heads of 128. Per row and head:
@@ -623,6 +674,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
                         (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
     if (rows16) {
       plain_epilogue_staged(p, acc, smem, scale, m0, nt, wave, lane);
+      return;
+    }
+  } else {
+    // an emit target is only accepted with aligned rows, so the 2-byte path below never needs it
+    const bool rows16 = (p.out_ld & 7) == 0 && (p.n_out & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+    if (rows16 || p.emit_out) {
+      swiglu_epilogue_staged(p, acc, smem, scale, m0, nt, wave, lane);
       return;
     }
   }

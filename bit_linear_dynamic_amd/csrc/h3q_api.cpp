@@ -409,8 +409,17 @@ struct QkArgs {
   const float *gamma_q, *gamma_k, *cos, *sin;
 };
 
+// Producer fusion: the SwiGLU epilogue also writes the next projection's base operand
+// (h3q_linear_swiglu_emit), or the call takes that operand ready-made (h3q_linear_prescaled).
+struct FuseArgs {
+  const float* emit_pqs;   // SwiGLU only: pqs of the next projection, fp32 [N/2]
+  uint16_t* emit_out;      // SwiGLU only: bf16 [S][N/2]
+  const uint16_t* xs;      // the base operand bf16 [S][K] given by the caller (x is then the LoRA input only)
+};
+
 h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
-                       int32_t adapter_id, float strength, uint32_t flags, uint16_t* out, const QkArgs* qk) {
+                       int32_t adapter_id, float strength, uint32_t flags, uint16_t* out, const QkArgs* qk,
+                       const FuseArgs* fuse = nullptr) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (!live(w)) return fail(H3Q_E_ARG, "linear: not a live weight handle");
   if (S != 0 && (!x || !out)) return fail(H3Q_E_ARG, "linear: null x or output");
@@ -452,7 +461,8 @@ h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float*
   if (dev != w->device) return fail(H3Q_E_ARG, "linear: weight lives on device %d, current is %d", w->device, dev);
 
   // workspace: [amax/ts_a : 256 B][act operand: S x K_pad bf16][t': S x r_pad bf16]
-  const bool direct_x = !w4a4 && !pqs && w->K == w->K_pad;  // x itself is the GEMM operand
+  const bool given_xs = fuse && fuse->xs;                   // the caller's xs is the GEMM operand
+  const bool direct_x = given_xs || (!w4a4 && !pqs && w->K == w->K_pad);  // no operand pass
   const size_t small = 256;
   const size_t act_bytes = direct_x ? 0 : static_cast<size_t>(round_up(S * w->K_pad * 2, 256));
   const size_t t_bytes = lora ? static_cast<size_t>(round_up(S * ad->r_pad * 2, 256)) : 0;
@@ -460,7 +470,8 @@ h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float*
   if (h3q_status st = workspace(dev, stream, small + act_bytes + t_bytes, &ws)) return st;
   uint32_t* amax_bits = reinterpret_cast<uint32_t*>(ws);
   float* ts_a = reinterpret_cast<float*>(ws + 4);
-  uint16_t* act = direct_x ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(ws + small);
+  uint16_t* act = given_xs ? const_cast<uint16_t*>(fuse->xs)
+                           : direct_x ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(ws + small);
   uint16_t* tbuf = lora ? reinterpret_cast<uint16_t*>(ws + small + act_bytes) : nullptr;
 
   hipError_t e = hipSuccess;
@@ -498,6 +509,11 @@ h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float*
   g.ts_dev = w4a4 ? ts_a : nullptr;
   g.out = out;
   g.out_ld = n_out;
+  if (fuse && fuse->emit_out) {
+    g.emit_pqs = fuse->emit_pqs;
+    g.emit_out = fuse->emit_out;
+    g.emit_ld = n_out;
+  }
   Epilogue epi = swiglu ? Epilogue::SwiGLU : Epilogue::Plain;
   if (qk) {
     g.qk_gamma_q = qk->gamma_q;
@@ -540,6 +556,42 @@ h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, c
   if (S != 0 && !aligned16(y)) return fail(H3Q_E_ARG, "qk_norm_rope: y must be 16-byte aligned");
   const QkArgs qk{q_width, rot_dim, eps, gamma_q, gamma_k, rope_cos, rope_sin};
   return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags, y, &qk);
+}
+
+h3q_status h3q_linear_swiglu_emit(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                                  int32_t adapter_id, float strength, uint32_t flags, uint16_t* h,
+                                  const float* pqs_next, uint16_t* xs_next) {
+  if (!live(w)) return fail(H3Q_E_ARG, "swiglu_emit: not a live weight handle");
+  if ((flags & ~static_cast<uint32_t>(H3Q_ACT_NVFP4)) != 0)
+    return fail(H3Q_E_ARG, "swiglu_emit: only H3Q_ACT_NVFP4 may be set (got flags 0x%x)", flags);
+  if (!gate_up(w)) return fail(H3Q_E_ARG, "swiglu_emit: needs a weight packed with H3Q_PACK_GATE_UP");
+  const int64_t F = w->N / 2;
+  if (F % 8 != 0) return fail(H3Q_E_SHAPE, "swiglu_emit: N/2 must be a multiple of 8 (N=%lld)", (long long)w->N);
+  if (!pqs_next || !xs_next) return fail(H3Q_E_ARG, "swiglu_emit: null pqs_next or xs_next");
+  if (S != 0 && (!aligned16(h) || !aligned16(xs_next) || !aligned16(pqs_next)))
+    return fail(H3Q_E_ARG, "swiglu_emit: h, xs_next and pqs_next must be 16-byte aligned");
+  {
+    const uintptr_t hb = reinterpret_cast<uintptr_t>(h), he = hb + static_cast<uintptr_t>(S * F * 2);
+    const uintptr_t sb = reinterpret_cast<uintptr_t>(xs_next), se = sb + static_cast<uintptr_t>(S * F * 2);
+    if (S > 0 && hb < se && sb < he) return fail(H3Q_E_ARG, "swiglu_emit: xs_next overlaps h");
+  }
+  const FuseArgs fa{pqs_next, xs_next, nullptr};
+  return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags | H3Q_EPI_SWIGLU, h, nullptr, &fa);
+}
+
+h3q_status h3q_linear_prescaled(void* stream, const uint16_t* x, const uint16_t* xs, int64_t S, h3q_weight w,
+                                int32_t adapter_id, float strength, uint16_t* y) {
+  if (!live(w)) return fail(H3Q_E_ARG, "linear_prescaled: not a live weight handle");
+  if (w->K % kGemmBK != 0)
+    return fail(H3Q_E_SHAPE, "linear_prescaled: K must be a multiple of %d (K=%lld)", kGemmBK, (long long)w->K);
+  if (S != 0 && (!xs || !aligned16(xs))) return fail(H3Q_E_ARG, "linear_prescaled: xs must be non-null and 16-byte aligned");
+  {
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(xs), xe = xb + static_cast<uintptr_t>(S * w->K * 2);
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(y), oe = ob + static_cast<uintptr_t>(S * w->N * 2);
+    if (S > 0 && xb < oe && ob < xe) return fail(H3Q_E_ARG, "linear_prescaled: output overlaps xs");
+  }
+  const FuseArgs fa{nullptr, nullptr, xs};
+  return linear_impl(stream, x, S, nullptr, w, adapter_id, strength, 0u, y, nullptr, &fa);
 }
 
 h3q_status h3q_linear(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,

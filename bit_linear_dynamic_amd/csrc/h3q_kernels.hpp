@@ -48,6 +48,11 @@ struct GemmParams {
   int32_t q_tiles;
   int32_t rope_half;        // rotated pairs per 128-wide head (rot_dim / 2)
   float qk_eps;
+  // SwiGLU epilogue only, optional: also write the next projection's base operand
+  // emit_out[s][n] = bf16(f32(h[s][n]) * emit_pqs[n]) (16-byte aligned rows, n_out % 8 == 0)
+  const float* emit_pqs;    // fp32 [n_out]
+  uint16_t* emit_out;       // bf16 [S][emit_ld] or null
+  int64_t emit_ld;
 };
 
 enum class Epilogue { Plain = 0, SwiGLU = 1, QkNormRope = 2 };

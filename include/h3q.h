@@ -116,6 +116,26 @@ h3q_status h3q_linear_swiglu(void* stream, const uint16_t* x, int64_t S, const f
 h3q_status h3q_linear_ex(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
                          int32_t adapter_id, float strength, uint32_t flags, uint16_t* out);
 
+/* Producer fusion across the MLP (FL2VA Turbo, "Implementation": a producer that emits the next
+ * projection's base input together with the exact bf16 LoRA input; on the pages' hardware it was
+ * bit-exact and 3.08% slower, and the runtime kept the materialized path).
+ *
+ * h3q_linear_swiglu_emit: h3q_linear_swiglu (flags: 0 or H3Q_ACT_NVFP4) whose epilogue also writes
+ *   xs_next[s][j] = bf16( f32(h[s][j]) * pqs_next[j] )
+ * -- the down projection's base operand, from the bf16 h it stores (so it equals what that projection
+ * would compute from h itself). h and xs_next: device bf16 [S][N/2]; pqs_next: device fp32 [N/2];
+ * all three 16-byte aligned, N/2 a multiple of 8; xs_next must not overlap h or x.
+ *
+ * h3q_linear_prescaled: h3q_linear with the base operand given: xs (device bf16 [S][K], 16-byte
+ * aligned) is the GEMM's activation operand as it stands, x (device bf16 [S][K]) only feeds the LoRA
+ * branch; there is no pre_quant_scale argument (it is inside xs). K must be a multiple of 64. With
+ * xs = bf16(x * pqs) the result is bit-identical to h3q_linear(x, pqs). Otherwise as h3q_linear. */
+h3q_status h3q_linear_swiglu_emit(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                                  int32_t adapter_id, float strength, uint32_t flags, uint16_t* h,
+                                  const float* pqs_next, uint16_t* xs_next);
+h3q_status h3q_linear_prescaled(void* stream, const uint16_t* x, const uint16_t* xs, int64_t S, h3q_weight w,
+                                int32_t adapter_id, float strength, uint16_t* y);
+
 /* Fused QKV projection followed by per-head Q/K RMSNorm and partial split-half rotary embedding
  * (MiniMax-H3 Ultra Fast, "Active optimization stack", attention projections: one fused QKV matrix
  * and one fused in-place Q/K RMSNorm + partial split-half RoPE; "Kernel path", item 2; 96 of the 128

@@ -16,8 +16,9 @@
 // and BK pqs values, and the
 // global latency is hidden by the bytes in flight rather than by compute. Each wave waits for its
 // own copies with one vmcnt and a barrier hands the stage over. The waves also write
-// xs = bf16(x * pqs) from the x operand they hold in registers, one 32 x 16 block per store, in
-// turn. Every vector-memory operation of the K loop is issued by the asm helpers of
+// xs = bf16(x * pqs), reading the tile back from LDS row by row so that every store covers whole
+// 128-byte row segments (8 rows per store of a wave; stores of 32-byte pieces of 32 rows, straight
+// from the MFMA operand registers, ran the write stream at a fraction of the read rate). Every vector-memory operation of the K loop is issued by the asm helpers of
 // h3q_device.hpp in a fixed number per wave per tile (copies without a real source re-read into a
 // spare LDS area, stores without a real target go past the buffer's end and are dropped), so one
 // vmcnt value per iteration waits exactly for the tile about to be read.
@@ -60,8 +61,8 @@ struct LdGeo {
   static constexpr int kCopiesA = NC * BK / 16;             // (at most CT*BK/16 per tile)
   static constexpr int kPqsLanes = BK / 16;                 // 16 bytes each, per wave
   static constexpr int CPT = kCopiesX + kCopiesA + 1;
-  static constexpr int kBlocks = RTM * (BK / 16);           // 32 x 16 xs blocks per tile
-  static constexpr int NS = (kBlocks + 3) / 4;              // xs stores per wave per tile
+  static constexpr int kChunks = RTM * 32 * (BK / 8);       // 16-byte xs chunks per tile
+  static constexpr int NS = (kChunks + 255) / 256;          // xs stores per wave per tile
   static_assert(ld_stage_bytes(RTM, NC, BK) == kStage, "stage layout");
   static_assert(kStages >= 3, "at least two tiles in flight");
   static_assert((L - 1) * CPT + L * NS < 64, "vmcnt range");
@@ -223,39 +224,37 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
         for (int j = 0; j < NC; ++j)
           if (static_cast<int>(wave) + 4 * j < ct)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      if (XS) {
-        // 32 x 16 blocks (i, kk) in turn: block i*(BK/16) + kk is stored by wave (that) % 4
-        float ps[8];
-        if (p.pqs) {
-          const f32x4 q0 = *reinterpret_cast<const f32x4*>(st + G::kP + (kk * 16 + h32 * 8) * 4);
-          const f32x4 q1 = *reinterpret_cast<const f32x4*>(st + G::kP + (kk * 16 + h32 * 8) * 4 + 16);
-          ps[0] = q0.x; ps[1] = q0.y; ps[2] = q0.z; ps[3] = q0.w;
-          ps[4] = q1.x; ps[5] = q1.y; ps[6] = q1.z; ps[7] = q1.w;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) ps[q] = 1.0f;
-        }
-        const uint32_t k = static_cast<uint32_t>(kt) * BK + kk * 16 + h32 * 8;
-#pragma unroll
-        for (int i = 0; i < RTM; ++i) {
-          if ((i * (BK / 16) + kk) % 4 != static_cast<int>(wave)) continue;
-          u32x4 out = scale_chunk(__builtin_bit_cast(u32x4, a[i]), ps);
-          if (k >= p.K) out = u32x4{0u, 0u, 0u, 0u};  // padding columns [K, K_pad) are zero
-          buf_store16(out, c.xs, (i * 32 + r32) * static_cast<uint32_t>(p.K_pad * 2) + h32 * 16,
-                      (static_cast<uint32_t>(kt) * BK + kk * 16) * 2);
-        }
-      }
     }
     if (XS) {
-      // pad this wave's stores of the tile to NS with stores past the buffer's end (dropped)
-      int mine = 0;
+      // xs = bf16(x * pqs) of the whole tile from its LDS copy, row-major: chunk q of the workgroup
+      // (16 bytes) is row q / (BK/8), chunk q % (BK/8), so one store of a wave covers 8 (BK = 64) or
+      // 16 (BK = 32) rows of full row segments. Every wave issues NS stores; chunks past the tile
+      // go past the buffer's end and are dropped.
 #pragma unroll
-      for (int i = 0; i < RTM; ++i)
+      for (int q = 0; q < NS; ++q) {
+        const uint32_t chunk = wave * 64 + lane + 256u * q;
+        const uint32_t row = chunk / (BK / 8), cc = chunk % (BK / 8);
+        const bool real = static_cast<int>(chunk) < G::kChunks;
+        u32x4 out = u32x4{0u, 0u, 0u, 0u};
+        if (real) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(st + G::kX + tile_offset<BK>(row, cc));
+          float ps[8];
+          if (p.pqs) {
+            const f32x4 q0 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32);
+            const f32x4 q1 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32 + 16);
+            ps[0] = q0.x; ps[1] = q0.y; ps[2] = q0.z; ps[3] = q0.w;
+            ps[4] = q1.x; ps[5] = q1.y; ps[6] = q1.z; ps[7] = q1.w;
+          } else {
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) mine += ((i * (BK / 16) + kk) % 4 == static_cast<int>(wave)) ? 1 : 0;
-#pragma unroll
-      for (int q = 0; q < NS; ++q)
-        if (q >= mine) buf_store16(u32x4{0u, 0u, 0u, 0u}, c.xs, 0x7ffffff0u, 0u);
+            for (int e = 0; e < 8; ++e) ps[e] = 1.0f;
+          }
+          out = scale_chunk(xv, ps);
+          if (static_cast<uint32_t>(kt) * BK + cc * 8 >= p.K) out = u32x4{0u, 0u, 0u, 0u};  // padding columns
+        }
+        // (the dummy offset stays out of range with the tile's column offset added: < 2^31 + 2^21)
+        buf_store16(out, c.xs, real ? row * static_cast<uint32_t>(p.K_pad * 2) + cc * 16 : 0x7ffffff0u,
+                    static_cast<uint32_t>(kt) * BK * 2);
+      }
     }
     s_cur = s_cur == NST - 1 ? 0 : s_cur + 1;
   }

@@ -15,10 +15,11 @@ conversion did") is ``merge_lora`` + ``quantize_nvfp4``. The AdaLN modulation cu
 (the adapter folded into a rank-24 table by the same K-concatenation) is ``adaln_table`` +
 ``adaln_apply``.
 
-Every function here is pinned by tests/test_oracle_*.py against things other than itself: the
-format's published code tables and torch's float8 conversion, exact rational arithmetic on small
-shapes, numpy's fp64 matmul, rank-1 closed forms and identities. Nothing in the oracle is
-"parity unpinned".
+Every function here is pinned by tests/test_oracle_*.py (pins in tests/pins.py) against things other
+than itself: the format's published code tables and torch's float8 conversion, exact rational
+arithmetic on small shapes, numpy's fp64 matmul, norms and complex arithmetic, rank-1 closed forms,
+the unfolded form of every folded formula, and identities. Nothing in the oracle is "parity
+unpinned".
 """
 from __future__ import annotations
 

@@ -141,3 +141,33 @@ def test_gemm_steps_inc_is_current():
     spec.loader.exec_module(gen)
     with open(os.path.join(csrc, "gemm_w4_steps.inc")) as f:
         assert f.read() == gen.render(), "gemm_w4_steps.inc is stale: run csrc/gen_gemm_steps.py"
+
+
+def test_side_entry_points_reject_bad_arguments(lib):
+    """The Q/K epilogue, merged route, producer fusion and AdaLN entry points validate before any
+    device work (dead handle, null or misshaped arguments)."""
+    bogus = ctypes.c_void_p(0x1234)
+    buf = np.zeros(4096, np.uint8)
+    p = ctypes.c_void_p(buf.ctypes.data)
+    f = ctypes.c_void_p(np.zeros(64, np.float32).ctypes.data)
+    assert lib.h3q_linear_qk_norm_rope(None, p, 1, None, bogus, -1, 0.0, 0, 256, 96, 1e-6, f, f, f, f, p) == h3q.H3Q_E_ARG
+    assert lib.h3q_merge_adapter(None, bogus, -1, 1.0, None, p, p, p, None) == h3q.H3Q_E_ARG
+    assert lib.h3q_linear_swiglu_emit(None, p, 1, None, bogus, -1, 0.0, 0, p, f, p) == h3q.H3Q_E_ARG
+    assert lib.h3q_linear_prescaled(None, p, p, 1, bogus, -1, 0.0, p) == h3q.H3Q_E_ARG
+    assert "live weight handle" in h3q.last_error()
+    # AdaLN table: null pointers, then shapes
+    assert lib.h3q_adaln_table(None, None, f, p, 1.0, 1, 5, 8, 8, 16, f) == h3q.H3Q_E_ARG
+    assert lib.h3q_adaln_table(None, f, f, None, 1.0, 1, 5, 8, 8, 16, f) == h3q.H3Q_E_ARG   # A needed for lora_rank > 0
+    for blocks, samples, emb, rb, rl in ((0, 5, 8, 8, 16), (1, 1, 8, 8, 16), (1, 5, 0, 8, 16), (1, 5, 8, 0, 16),
+                                         (1, 5, 8, 8, 33), (1, 5, 8, 40, 32), (70000, 5, 8, 8, 16)):
+        assert lib.h3q_adaln_table(None, f, f, p, 1.0, blocks, samples, emb, rb, rl, f) == h3q.H3Q_E_SHAPE, \
+            (blocks, samples, emb, rb, rl)
+    assert lib.h3q_adaln_table(None, f, f, p, math.inf, 1, 5, 8, 8, 16, f) == h3q.H3Q_E_ARG
+    # AdaLN apply: null pointers, then shapes, then alignment
+    assert lib.h3q_adaln_apply(None, None, None, f, f, 1, 1, 16, 5, 24, f) == h3q.H3Q_E_ARG
+    for T, blocks, rows, samples, R in ((0, 1, 16, 5, 24), (9, 1, 16, 5, 24), (1, 0, 16, 5, 24), (1, 1, -1, 5, 24),
+                                        (1, 1, 16, 1, 24), (1, 1, 16, 5, 20), (1, 1, 16, 5, 72), (1, 1, 16, 5, 0)):
+        assert lib.h3q_adaln_apply(None, p, None, f, f, T, blocks, rows, samples, R, f) == h3q.H3Q_E_SHAPE, \
+            (T, blocks, rows, samples, R)
+    odd = ctypes.c_void_p(buf.ctypes.data + 2)
+    assert lib.h3q_adaln_apply(None, odd, None, f, f, 1, 1, 16, 5, 24, f) == h3q.H3Q_E_ARG

@@ -6,9 +6,10 @@
 // blocks) and e (E values) are sampled at S points t_i = i / (S - 1); v_b is tabulated there and
 // interpolated linearly.
 //
-// adaln_table_kernel: one wave per pair of samples of one block; lanes split the E-wide dot products
-//   A_b[j] . silu(e_i) (fp32, silu(z) = z / (1 + exp(-z))), then a butterfly reduction. A one-off per
-//   adapter and strength: 2 * blocks * S * rl * E flops (2.2 GFLOP for 50 blocks of rank 16).
+// adaln_table_kernel: one wave per 4 samples of one block; lanes split the E-wide dot products
+//   A_b[j] . silu(e_i) (fp32, silu(z) = z / (1 + exp(-z))) in 8-column chunks, then a butterfly
+//   reduction. A one-off per adapter and strength: 2 * blocks * S * rl * E flops (4.4 GFLOP for 50
+//   blocks of rank 16).
 // adaln_apply_kernel: a stream over [W_p | B] (bf16 [rows][R] per block, R = rb + rl): one row per
 //   thread, R / 8 16-byte loads, T outputs per row from the T interpolated v's kept in LDS. Bytes per
 //   call: blocks * rows * (2 R + 4 [bias] + 4 T [out]) -- HBM-bound.
@@ -23,30 +24,70 @@ constexpr int kMaxRl = 32;
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+constexpr int kSamplesPerWave = 4;
+
+// 8 consecutive values of one embedding row through silu (zeros past E).
+__device__ __forceinline__ void silu8(const float* row, int E, int k0, float (&s)[8]) {
+  if (k0 + 8 <= E && (E & 3) == 0) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + k0);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + k0 + 4);
+    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w; s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = k0 + e < E ? row[k0 + e] : 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = silu_f32(s[e]);
+}
+
+// 8 consecutive bf16 of one A row as fp32 (zeros past E).
+__device__ __forceinline__ void a8(const uint16_t* row, int E, int k0, float (&a)[8]) {
+  if (k0 + 8 <= E && (E & 7) == 0) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(row + k0);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[2 * e] = bf16_bits_to_f32(ws[e] & 0xffffu);
+      a[2 * e + 1] = bf16_bits_to_f32(ws[e] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = k0 + e < E ? bf16_bits_to_f32(row[k0 + e]) : 0.0f;
+  }
+}
+
+// One wave per kSamplesPerWave samples of one block: lane l takes the 8-column chunks l, l + 64, ...
+// of the embedding rows and of every A_b row (16-byte loads), so each A value loaded serves all the
+// wave's samples; then a butterfly sum over the lanes.
 __global__ __launch_bounds__(256) void adaln_table_kernel(AdalnTableParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y;
-  const int i0 = (blockIdx.x * 4 + wave) * 2;
+  const int i0 = (blockIdx.x * 4 + wave) * kSamplesPerWave;
   if (i0 >= p.S) return;
-  const bool two = i0 + 1 < p.S;
+  const int ns = min(kSamplesPerWave, p.S - i0);
   const int R = p.rb + p.rl;
-  float acc[2][kMaxRl];
+  float acc[kSamplesPerWave][kMaxRl];
 #pragma unroll
-  for (int j = 0; j < kMaxRl; ++j) acc[0][j] = acc[1][j] = 0.0f;
-  const float* e0 = p.emb + static_cast<int64_t>(i0) * p.E;
-  const float* e1 = two ? e0 + p.E : e0;
+  for (int s = 0; s < kSamplesPerWave; ++s)
+#pragma unroll
+    for (int j = 0; j < kMaxRl; ++j) acc[s][j] = 0.0f;
   const uint16_t* Ab = p.A + static_cast<int64_t>(b) * p.rl * p.E;
-  for (int k = lane; k < p.E; k += 64) {
-    const float s0 = silu_f32(e0[k]), s1 = silu_f32(e1[k]);
-    const uint16_t* ap = Ab + k;  // walks down column k of A_b
+  for (int k0 = lane * 8; k0 < p.E; k0 += 64 * 8) {
+    float sv[kSamplesPerWave][8];
+#pragma unroll
+    for (int s = 0; s < kSamplesPerWave; ++s) silu8(p.emb + static_cast<int64_t>(min(i0 + s, p.S - 1)) * p.E, p.E, k0, sv[s]);
+    const uint16_t* ap = Ab;
 #pragma unroll
     for (int j = 0; j < kMaxRl; ++j) {
       if (j < p.rl) {
-        const float a = bf16_bits_to_f32(*ap);
+        float a[8];
+        a8(ap, p.E, k0, a);
         ap += p.E;
-        acc[0][j] = fmaf(a, s0, acc[0][j]);
-        acc[1][j] = fmaf(a, s1, acc[1][j]);
+#pragma unroll
+        for (int s = 0; s < kSamplesPerWave; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[s][j] = fmaf(a[e], sv[s][e], acc[s][j]);
       }
     }
   }
@@ -54,13 +95,14 @@ __global__ __launch_bounds__(256) void adaln_table_kernel(AdalnTableParams p) {
   for (int j = 0; j < kMaxRl; ++j) {
     if (j < p.rl) {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        acc[0][j] += __shfl_xor(acc[0][j], off);
-        acc[1][j] += __shfl_xor(acc[1][j], off);
-      }
+      for (int s = 0; s < kSamplesPerWave; ++s)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc[s][j] += __shfl_xor(acc[s][j], off);
     }
   }
-  for (int s = 0; s < (two ? 2 : 1); ++s) {
+#pragma unroll
+  for (int s = 0; s < kSamplesPerWave; ++s) {
+    if (s >= ns) break;
     float* row = p.table + (static_cast<int64_t>(b) * p.S + i0 + s) * R;
     if (lane < p.rb) row[lane] = p.u[static_cast<int64_t>(i0 + s) * p.rb + lane];
 #pragma unroll
@@ -114,7 +156,8 @@ __global__ __launch_bounds__(kApplyThreads) void adaln_apply_kernel(AdalnApplyPa
 }  // namespace
 
 hipError_t launch_adaln_table(const AdalnTableParams& p, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>((p.S + 7) / 8), static_cast<uint32_t>(p.blocks));
+  const int per_wg = 4 * kSamplesPerWave;
+  const dim3 grid(static_cast<uint32_t>((p.S + per_wg - 1) / per_wg), static_cast<uint32_t>(p.blocks));
   hipLaunchKernelGGL(adaln_table_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }

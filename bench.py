@@ -229,6 +229,51 @@ def producer_fusion(projs, stream, calls=5):
     return out
 
 
+def w4a4_gate_up(projs, stream, calls=5):
+    """The W4A4 variant on the fused gate/up projection at the bench's S: activations quantized to
+    NVFP4 per call for the base GEMM, LoRA on the original x, SiLU(gate) * up in the epilogue. Per
+    call: wall time, and each kernel's share from the library's HIP events (the quantizer's two passes
+    read x twice and write the decoded operand)."""
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+    from bit_linear_dynamic_amd import workloads as wl
+
+    d = next((d for d in projs if d["p"].name == "gate_up"), None)
+    if d is None:
+        return None
+    p = d["p"]
+    S = d["x"].shape[0]
+    h = torch.empty((S, p.N // 2), dtype=torch.bfloat16, device=d["x"].device)
+    flags = h3q.H3Q_ACT_NVFP4 | h3q.H3Q_EPI_SWIGLU
+
+    def call():
+        h3q.h3q_linear_ex(d["x"], d["pqs"], d["handle"], 1, 1.0, flags, out=h, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    h3q.h3q_timing_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(calls):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    call_ms = a.elapsed_time(b) / calls
+    g, gn = h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM)
+    q, qn = h3q.h3q_timing_get(h3q.H3Q_KERNEL_ACT_QUANT)
+    l, ln = h3q.h3q_timing_get(h3q.H3Q_KERNEL_LORA_DOWN)
+    h3q.h3q_timing_enable(False)
+    g, q, l = g / gn, q / qn, l / ln
+    K_pad = (p.K + 63) // 64 * 64
+    q_bytes = 2 * S * p.K * 2 + S * K_pad * 2 + p.K * 4
+    return {"S": S, "projection": [p.N, p.K, p.rank], "call_ms": round(call_ms, 4),
+            "effective_tflops": round(wl.effective_flops(S, p) / (call_ms * 1e-3) / 1e12, 1),
+            "gemm_ms": round(g, 4), "gemm_tflops": round(2 * S * p.N * (p.K + p.rank) / (g * 1e-3) / 1e12, 1),
+            "act_quant_ms": round(q, 4), "act_quant_bytes": q_bytes,
+            "act_quant_GBps": round(q_bytes / (q * 1e-3) / 1e9, 1), "lora_down_ms": round(l, 4)}
+
+
 def adaln_curve(stream, device, reps=50):
     """The AdaLN modulation curve of all 50 blocks ([96768, 24] each, 1025 samples, rank 8 + 16) at
     T = 2 times per call: apply time and its HBM rate (bytes = blocks * rows * (2 R + 4 + 4 T)), and
@@ -360,6 +405,7 @@ def main():
     mvd = None if args.timed_only else merged_vs_dynamic(projs, stream)
     adaln = None if args.timed_only else adaln_curve(stream, device)
     fusion = None if args.timed_only else producer_fusion(projs, stream)
+    w4a4 = None if args.timed_only else w4a4_gate_up(projs, stream)
 
     cpu = None
     if not args.no_cpu:
@@ -396,6 +442,7 @@ def main():
         "merged_vs_dynamic": mvd,
         "adaln_curve": adaln,
         "mlp_producer_fusion": fusion,
+        "w4a4_swiglu_gate_up": w4a4,
         "cpu_baseline": cpu,
     }
     for d in projs:

@@ -15,8 +15,9 @@
 //     (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) * d, d = E4M3(s_b) * ts, all exact products; on a tie
 //     the comparison direction picks the neighbour with the even mantissa bit.
 // The same quantizer serves the merged-weight route on an fp32 input (ActQuantParams::xf: v = the
-// input itself). Two passes: a grid-wide amax (atomic max on the fp32 bit pattern, exact and order-free), then one
-// thread per 16-element block. The second pass can also write the decoded activation
+// input itself). Two passes: a grid-wide amax (rows over workgroups, 16-byte chunks over threads;
+// atomic max on the fp32 bit pattern, exact and order-free), then one thread per 16-element block;
+// without pqs, v = x * 1 = x in both. The second pass can also write the decoded activation
 // E2M1 * E4M3 (exact bf16, tensor scale left to the GEMM epilogue) as the GEMM's operand.
 #include "h3q_device.hpp"
 #include "h3q_kernels.hpp"
@@ -25,29 +26,43 @@ namespace h3q {
 
 namespace {
 
-__device__ __forceinline__ float prescaled(uint32_t xbits, const float* pqs, int64_t k) {
-  const float x = bf16_bits_to_f32(xbits);
-  return pqs ? x * pqs[k] : x;
-}
-
 __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 
+// Grid-strided over rows, threads strided over the 16-byte chunks of a row (no division per element).
 __global__ __launch_bounds__(256) void amax_kernel(ActQuantParams p) {
-  const int64_t total = p.S * p.K;
   float m = 0.0f;
-  if (p.xf) {  // fp32 input (K % 16 == 0, so quads never cross a row)
-    for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < total;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x * 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.xf + i);
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  if (p.xf) {  // fp32 input: 4 values per chunk (K % 16 == 0)
+    const int64_t chunks = p.K / 4;
+    for (int64_t row = blockIdx.x; row < p.S; row += gridDim.x) {
+      const f32x4* xr = reinterpret_cast<const f32x4*>(p.xf + row * p.K);
+      for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
+        const f32x4 v = xr[c];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      }
     }
-  } else {
-    for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 2; i < total;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x * 2) {
-      const uint32_t two = *reinterpret_cast<const uint32_t*>(p.x + i);  // K even: pairs stay in a row
-      const int64_t k = i % p.K;
-      m = fmaxf(m, fabsf(prescaled(two & 0xffffu, p.pqs, k)));
-      m = fmaxf(m, fabsf(prescaled(two >> 16, p.pqs, k + 1)));
+  } else {  // bf16 input times pqs: 8 values per chunk
+    const int64_t chunks = p.K / 8;
+    for (int64_t row = blockIdx.x; row < p.S; row += gridDim.x) {
+      const u32x4* xr = reinterpret_cast<const u32x4*>(p.x + row * p.K);
+      for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
+        const u32x4 v = xr[c];
+        float pq[8];
+        if (p.pqs) {
+          const f32x4 q0 = *reinterpret_cast<const f32x4*>(p.pqs + c * 8);
+          const f32x4 q1 = *reinterpret_cast<const f32x4*>(p.pqs + c * 8 + 4);
+          pq[0] = q0.x; pq[1] = q0.y; pq[2] = q0.z; pq[3] = q0.w;
+          pq[4] = q1.x; pq[5] = q1.y; pq[6] = q1.z; pq[7] = q1.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pq[e] = 1.0f;
+        }
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] & 0xffffu) * pq[2 * e]));
+          m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] >> 16) * pq[2 * e + 1]));
+        }
+      }
     }
   }
   // wave64 reduction, then one atomic per wave (|v| >= 0: fp32 bit patterns order as unsigned)
@@ -105,10 +120,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(ActQuantParams p) {
       const u32x4 x0 = *reinterpret_cast<const u32x4*>(p.x + row * p.K + k0);
       const u32x4 x1 = *reinterpret_cast<const u32x4*>(p.x + row * p.K + k0 + 8);
       const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float pq[16];
+      if (p.pqs) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 f = *reinterpret_cast<const f32x4*>(p.pqs + k0 + 4 * q);
+          pq[4 * q] = f.x;
+          pq[4 * q + 1] = f.y;
+          pq[4 * q + 2] = f.z;
+          pq[4 * q + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pq[i] = 1.0f;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        v[2 * i] = prescaled(xw[i] & 0xffffu, p.pqs, k0 + 2 * i);
-        v[2 * i + 1] = prescaled(xw[i] >> 16, p.pqs, k0 + 2 * i + 1);
+        v[2 * i] = bf16_bits_to_f32(xw[i] & 0xffffu) * pq[2 * i];
+        v[2 * i + 1] = bf16_bits_to_f32(xw[i] >> 16) * pq[2 * i + 1];
       }
     }
     float amax_b = 0.0f;
@@ -146,10 +175,8 @@ hipError_t launch_act_quant(const ActQuantParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, stream, p.amax_bits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = p.S * p.K;
-  if (total > 0) {
-    int64_t grid = (total / 2 + 255) / 256;
-    if (grid > 256 * 32) grid = 256 * 32;
+  if (p.S > 0) {
+    const int64_t grid = p.S < 256 * 16 ? p.S : 256 * 16;  // one or more whole rows per workgroup
     hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

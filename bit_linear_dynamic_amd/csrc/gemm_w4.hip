@@ -730,6 +730,7 @@ hipError_t launch_variant(const GemmParams& p0, hipStream_t stream) {
     p.act = p0.act + r0 * p0.act_ld;
     p.lora_t = p0.lora_t ? p0.lora_t + r0 * p0.lora_t_ld : nullptr;
     p.out = p0.out + r0 * p0.out_ld;
+    if (p.emit_out) p.emit_out = p0.emit_out + r0 * p0.emit_ld;
     p.m_tiles = static_cast<int32_t>((p.S + BM - 1) / BM);
     const int64_t items = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
     const int64_t grid = (items + 7) / 8 * 8;

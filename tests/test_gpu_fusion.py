@@ -114,6 +114,29 @@ def test_mlp_chain_full_s8192():
         dn.free()
 
 
+def test_emit_across_row_ranges():
+    """K = 16384 puts more than 2 GiB of activation in S = 65836 rows, so the GEMM runs as two row
+    ranges (32-bit buffer offsets); the emitted operand of the second range must land in its own rows:
+    the fused chain stays bit-identical to the unfused one on every row."""
+    S, K, F, D = 65836, 16384, 256, 128
+    say(f"fusion chain across row ranges S={S} K={K}")
+    gu = Proj(2 * F, K, 1900, gate_up=True)
+    dn = Proj(D, F, 1901)
+    try:
+        gu.add_adapter(1, 16, 16.0, 1902, 1903)
+        dn.add_adapter(1, 16, 16.0, 1904, 1905)
+        x = synth.activation(S, K, 1906, "cuda")
+        pqs_gu = synth.pre_quant_scale(K, 1907, "cuda")
+        pqs_dn = synth.pre_quant_scale(F, 1908, "cuda")
+        h, y, h2, xs, y2 = chain(gu, dn, x, pqs_gu, pqs_dn, 1, 1.0)
+        assert torch.equal(h, h2)
+        assert torch.equal(y, y2), "fused chain differs across the row ranges"
+        say("  h and y bit-identical on all rows")
+    finally:
+        gu.free()
+        dn.free()
+
+
 def test_fusion_argument_errors():
     gu = Proj(2 * 36, 64, 1800, gate_up=True)     # F = 36: not a multiple of 8
     plain = Proj(64, 64, 1801)

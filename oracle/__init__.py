@@ -72,6 +72,9 @@ def _declare(lib):
     lib.orc_adaln_table.restype = None
     lib.orc_adaln_apply.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
     lib.orc_adaln_apply.restype = None
+    lib.orc_f32_to_bf16.argtypes, lib.orc_f32_to_bf16.restype = [f32], ctypes.c_uint16
+    lib.orc_linear_mirror.argtypes = [vp, i64, i64, vp, vp, vp, f32, i64, vp, vp, i64, f64, f64, vp]
+    lib.orc_linear_mirror.restype = i32
     lib.orc_num_threads.argtypes, lib.orc_num_threads.restype = [], i32
     return lib
 
@@ -245,6 +248,30 @@ def adaln_apply(M_bits, bias, table, t, lib=None) -> np.ndarray:
     (lib or load()).orc_adaln_apply(_ptr(M_bits), _ptr(bias), _ptr(table), _ptr(t), t.shape[0], blocks, rows, S, R,
                                     _ptr(out))
     return out
+
+
+def f32_to_bf16(v: float, lib=None) -> int:
+    """bf16 bit pattern of an fp32 value, round to nearest even."""
+    return int((lib or load()).orc_f32_to_bf16(float(v)))
+
+
+def linear_mirror(x_bits, pqs, codes, scales, ts, A_bits=None, B_bits=None, rank=0, alpha=0.0, strength=0.0,
+                  lib=None) -> np.ndarray:
+    """Diagnostic: bf16 bits [M][N] of the linear with the GPU path's declared rounding points (see
+    oracle.cpp, orc_linear_mirror)."""
+    x_bits = _c(x_bits, np.uint16)
+    M, K = x_bits.shape
+    codes = _c(codes, np.uint8)
+    N = codes.shape[0]
+    y = np.empty((M, N), np.uint16)
+    pqs, scales = _c(pqs, np.float32), _c(scales, np.uint8)
+    A_bits, B_bits = _c(A_bits, np.uint16), _c(B_bits, np.uint16)
+    rc = (lib or load()).orc_linear_mirror(_ptr(x_bits), M, K, _ptr(pqs), _ptr(codes), _ptr(scales), float(ts), N,
+                                           _ptr(A_bits), _ptr(B_bits), int(rank), float(alpha), float(strength),
+                                           _ptr(y))
+    if rc != 0:
+        raise ValueError("orc_linear_mirror: bad shape")
+    return y
 
 
 def num_threads(lib=None) -> int:

@@ -365,6 +365,55 @@ void orc_adaln_apply(const uint16_t* M, const float* bias, const double* table, 
   }
 }
 
+// fp32 -> bf16 bit pattern, round to nearest with ties to even (finite inputs): add 0x7FFF plus the
+// lowest kept bit, then drop the low half-word.
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Mirror mode (a diagnostic beside the graded fp64 oracle): the linear with the rounding points the
+// GPU path declares, everything else exact in fp64 --
+//   xs  = bf16( f32(x * pqs) )                         the base operand
+//   f   = f32( strength * alpha / (rank * ts) )
+//   t'  = bf16( f * f32( sum_k x * A[j] ) )             the folded LoRA-down output
+//   acc = sum_k xs * (E2M1 * E4M3) + sum_j t' * B        (fp64)
+//   y   = bf16( f32(ts) * f32(acc) )
+// so the GPU's y differs from it only by the order and precision of its fp32 accumulation. Same
+// arguments as orc_linear (W4A16 only); y_bits: bf16 bit patterns [M][N].
+int orc_linear_mirror(const uint16_t* x, int64_t M, int64_t K, const float* pqs, const uint8_t* codes,
+                      const uint8_t* scales, float ts, int64_t N, const uint16_t* A, const uint16_t* B,
+                      int64_t rank, double alpha, double strength, uint16_t* y_bits) {
+  if (K % 16 != 0 || M < 0 || N < 0 || rank < 0) return -1;
+  std::vector<double> Wq(static_cast<size_t>(N * K));
+  orc_dequant(codes, scales, 1.0, N, K, Wq.data());
+  const bool lora = (A != nullptr && B != nullptr && rank > 0);
+  const float f = lora ? static_cast<float>(strength * alpha / (static_cast<double>(rank) * static_cast<double>(ts))) : 0.0f;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m) {
+    std::vector<double> xs(static_cast<size_t>(K));
+    for (int64_t k = 0; k < K; ++k) {
+      const double xv = bf16_to_double(x[m * K + k]);
+      xs[k] = pqs ? bf16_to_double(orc_f32_to_bf16(static_cast<float>(xv * static_cast<double>(pqs[k])))) : xv;
+    }
+    std::vector<double> tq(static_cast<size_t>(lora ? rank : 0));
+    for (int64_t j = 0; lora && j < rank; ++j) {
+      double s = 0.0;
+      for (int64_t k = 0; k < K; ++k) s += bf16_to_double(x[m * K + k]) * bf16_to_double(A[j * K + k]);
+      tq[j] = bf16_to_double(orc_f32_to_bf16(f * static_cast<float>(s)));
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += xs[k] * Wq[n * K + k];
+      for (int64_t j = 0; lora && j < rank; ++j) acc += tq[j] * bf16_to_double(B[n * rank + j]);
+      y_bits[m * N + n] = orc_f32_to_bf16(ts * static_cast<float>(acc));
+    }
+  }
+  return 0;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -559,4 +559,52 @@ def pin_adaln_interpolation(lib):
         np.testing.assert_allclose(at(t), (1 - th) * exact(i) + th * exact(i + 1), rtol=1e-12, atol=1e-12)
 
 
+def pin_bf16_rne_vs_torch(lib):
+    """The oracle's fp32 -> bf16 rounding against torch's conversion (round to nearest even) on random
+    magnitudes and on constructed ties of both parities."""
+    rng = np.random.default_rng(37)
+    vals = (rng.standard_normal(4000) * 10.0 ** rng.integers(-20, 20, 4000)).astype(np.float32)
+    hi = rng.integers(0, 0x7F7F, 400, dtype=np.uint32) << 16
+    ties = (hi | 0x8000).view(np.float32)  # exactly halfway: the even neighbour must win
+    near = (hi | 0x7FFF).view(np.float32)
+    allv = np.concatenate([vals, ties, near, -ties, np.array([0.0, -0.0, 1.0, 3.0e38], np.float32)])
+    want = torch.from_numpy(allv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16(float(v), lib=lib) for v in allv], np.uint16)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def pin_mirror_exact_cases(lib):
+    """Mirror mode where every declared rounding is exact: identity activation with power-of-two pqs
+    and ts gives bf16(ts Wq pqs) bit for bit; zero weight codes with a dyadic rank-1 adapter on a
+    one-hot row give bf16(c a_k b_n) bit for bit."""
+    rng = np.random.default_rng(38)
+    K, N = 48, 6
+    codes, scales, _ = random_nvfp4(N, K, rng, lib=lib)
+    ts = 0.125
+    pqs = (2.0 ** rng.integers(-1, 2, K)).astype(np.float32)
+    x = bits_of(np.eye(K))
+    got = oracle.linear_mirror(x, pqs, codes, scales, ts, lib=lib)
+    want = bits_of(decode_independent(codes, scales, ts).T * pqs.astype(np.float64)[:, None])
+    assert np.array_equal(got, want)
+    k = 11
+    pqs[k] = 2.0  # the adapter branch must see x itself, not x * pqs
+    a = rng.integers(-4, 5, K) / 8.0
+    b = rng.integers(-4, 5, N) / 8.0
+    zc = np.zeros_like(codes)
+    got = oracle.linear_mirror(bits_of(np.eye(K)[k:k + 1]), pqs, zc, scales, 0.25, bits_of(a[None, :]),
+                               bits_of(b[:, None]), 1, 2.0, 0.25, lib=lib)
+    assert np.array_equal(got[0], bits_of(0.5 * a[k] * b))
+
+
+def pin_mirror_within_bar(lib):
+    """On random inputs the mirror differs from the exact oracle only by its roundings: within the
+    parity bar, and above zero (the roundings are really applied)."""
+    rng = np.random.default_rng(39)
+    x, pqs, codes, scales, ts, A, B = _lora_case(rng, 7, 96, 40, 8, lib)
+    ref = oracle.linear(x, pqs, codes, scales, ts, A, B, 8, 4.0, 0.75, lib=lib)
+    got = bf16_values(oracle.linear_mirror(x, pqs, codes, scales, ts, A, B, 8, 4.0, 0.75, lib=lib))
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 1e-5 < err < 4e-3, err
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

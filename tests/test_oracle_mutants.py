@@ -36,7 +36,7 @@ MUTANTS = [
     ("pqs_dropped", "bf16_to_double(x[m * K + k]) * (pqs ? static_cast<double>(pqs[k]) : 1.0)",
      "bf16_to_double(x[m * K + k])", 0),
     ("lora_sees_prescaled_x", "s += bf16_to_double(x[m * K + k]) * bf16_to_double(A[j * K + k]);",
-     "s += act[m * K + k] * bf16_to_double(A[j * K + k]);", 0),
+     "s += act[m * K + k] * bf16_to_double(A[j * K + k]);", 1),
     ("alpha_over_rank_dropped", "strength * alpha / static_cast<double>(rank)", "strength", 0),
     ("rank_over_alpha", "strength * alpha / static_cast<double>(rank)", "strength * static_cast<double>(rank) / alpha", 0),
     ("B_transposed", "bf16_to_double(B[n * rank + j])", "bf16_to_double(B[j * N + n])", 0),
@@ -72,6 +72,14 @@ MUTANTS = [
     ("adaln_interp_swapped", "v[q] = (1.0 - th) * t0[q] + th * t1[q];", "v[q] = th * t0[q] + (1.0 - th) * t1[q];", 0),
     ("adaln_grid_S", "const double p = tt * static_cast<double>(S - 1);", "const double p = tt * static_cast<double>(S);", 0),
     ("adaln_bias_dropped", "double acc = bias ? static_cast<double>(bias[b * rows + r]) : 0.0;", "double acc = 0.0;", 0),
+    ("bf16_truncates", "u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;", 0),
+    ("bf16_ties_up", "u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x8000u;", 0),
+    ("mirror_ts_dropped", "y_bits[m * N + n] = orc_f32_to_bf16(ts * static_cast<float>(acc));",
+     "y_bits[m * N + n] = orc_f32_to_bf16(static_cast<float>(acc));", 0),
+    ("mirror_f_keeps_ts", "strength * alpha / (static_cast<double>(rank) * static_cast<double>(ts))",
+     "strength * alpha / static_cast<double>(rank)", 0),
+    ("mirror_lora_sees_xs", "s += bf16_to_double(x[m * K + k]) * bf16_to_double(A[j * K + k]);\n      tq[j]",
+     "s += xs[k] * bf16_to_double(A[j * K + k]);\n      tq[j]", 0),
     ("rmsnorm_touches_v", "for (int64_t c0 = 0; c0 < 2 * qw; c0 += hd) {", "for (int64_t c0 = 0; c0 < N; c0 += hd) {", 0),
 ]
 
@@ -82,11 +90,18 @@ def mutant_libs():
     tmp = tempfile.mkdtemp(prefix="oracle_mutants_")
 
     def make(m):
-        name, old, new, _ = m
-        assert src.count(old) >= 1, f"mutant {name}: pattern not found"
+        name, old, new, which = m
+        assert src.count(old) >= max(1, which), f"mutant {name}: pattern not found"
+        if which == 0:
+            text = src.replace(old, new)
+        else:  # only the which-th occurrence
+            at = -1
+            for _ in range(which):
+                at = src.index(old, at + 1)
+            text = src[:at] + new + src[at + len(old):]
         path = os.path.join(tmp, f"{name}.cpp")
         with open(path, "w") as f:
-            f.write(src.replace(old, new))
+            f.write(text)
         return name, oracle.build(os.path.join(tmp, f"lib{name}.so"), src=path)
 
     with ThreadPoolExecutor(max_workers=4) as ex:

@@ -274,6 +274,43 @@ def w4a4_gate_up(projs, stream, calls=5):
             "act_quant_GBps": round(q_bytes / (q * 1e-3) / 1e9, 1), "lora_down_ms": round(l, 4)}
 
 
+def mfma_ceiling(stream, device, gemm_achieved):
+    """The matrix-core rate the board sustains under its power limit (h3q_mfma_loop: rotating operand
+    pairs, two waves per SIMD, no memory traffic), on activation-like bf16 N(0, 1) operands against
+    decoded-weight-like ones (E2M1 value times an E4M3 block scale, exact in bf16); the median of three
+    ~20 ms runs. The GEMM's rate is then also read against this practical ceiling."""
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+    from bit_linear_dynamic_amd import synth
+
+    ops_a = synth.normal((8, 256, 8), 1.0, synth.seed_of(11, 0, 0), device, torch.bfloat16)
+    e2m1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed(synth.seed_of(11, 0, 1))
+    mag = e2m1[torch.randint(0, 8, (8, 256, 8), generator=g, device=device)]
+    sign = torch.randint(0, 2, (8, 256, 8), generator=g, device=device) * 2.0 - 1.0
+    scale = torch.exp2(torch.randint(-8, -5, (8, 256, 1), generator=g, device=device).float()) * \
+        (1.0 + torch.randint(0, 8, (8, 256, 1), generator=g, device=device).float() / 8.0)
+    ops_b = (sign * mag * scale).to(torch.bfloat16)
+    wgs = 2 * torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    flop_per_iter = wgs * 4 * 64 * 32768
+    sink = h3q.h3q_mfma_loop(ops_a, ops_b, 100, wgs, stream=stream)
+    iters = max(1, int(0.02 * 1.7e15 / flop_per_iter))
+    runs = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        h3q.h3q_mfma_loop(ops_a, ops_b, iters, wgs, sink=sink, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        runs.append(flop_per_iter * iters / (a.elapsed_time(b) * 1e-3) / 1e12)
+    tf = sorted(runs)[1]
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "gemm_frac_of_loop": round(gemm_achieved / tf, 4), "workgroups": wgs, "iters": iters}
+
+
 def adaln_curve(stream, device, reps=50):
     """The AdaLN modulation curve of all 50 blocks ([96768, 24] each, 1025 samples, rank 8 + 16) at
     T = 2 times per call: apply time and its HBM rate (bytes = blocks * rows * (2 R + 4 + 4 T)), and
@@ -406,6 +443,7 @@ def main():
     adaln = None if args.timed_only else adaln_curve(stream, device)
     fusion = None if args.timed_only else producer_fusion(projs, stream)
     w4a4 = None if args.timed_only else w4a4_gate_up(projs, stream)
+    ceiling = None if args.timed_only else mfma_ceiling(stream, device, achieved)
 
     cpu = None
     if not args.no_cpu:
@@ -443,6 +481,7 @@ def main():
         "adaln_curve": adaln,
         "mlp_producer_fusion": fusion,
         "w4a4_swiglu_gate_up": w4a4,
+        "mfma_loop_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     for d in projs:

@@ -52,6 +52,7 @@ def _declare(lib):
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_dequant": [vp, vp, vp],
         "h3q_merge_adapter": [vp, vp, i32, f32, vp, vp, vp, vp, vp],
+        "h3q_mfma_loop": [vp, vp, vp, i32, i32, vp],
         "h3q_linear_swiglu_emit": [vp, vp, i64, vp, vp, i32, f32, u32, vp, vp, vp],
         "h3q_linear_prescaled": [vp, vp, vp, i64, vp, i32, f32, vp],
         "h3q_adaln_table": [vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, vp],
@@ -323,6 +324,18 @@ def h3q_adaln_apply(M, bias, table, t, out=None, stream=None):
                                  _dev_ptr(table, torch.float32, "table"), _dev_ptr(t, torch.float32, "t"), T, blocks,
                                  rows, S, R, _dev_ptr(out, torch.float32, "out")))
     return out
+
+
+def h3q_mfma_loop(ops_a, ops_b, iters: int, workgroups: int, sink=None, stream=None):
+    """Pure matrix-core loop (measurement aid). ops_a, ops_b: device bf16 [8][256][8]. Returns the sink."""
+    import torch
+    if tuple(ops_a.shape) != (8, 256, 8) or tuple(ops_b.shape) != (8, 256, 8):
+        raise ValueError("ops_a and ops_b must be [8][256][8]")
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device=ops_a.device) if sink is None else sink
+    _check(lib().h3q_mfma_loop(_stream(stream), _dev_ptr(ops_a, torch.bfloat16, "ops_a"),
+                               _dev_ptr(ops_b, torch.bfloat16, "ops_b"), int(iters), int(workgroups),
+                               _dev_ptr(sink, torch.float32, "sink")))
+    return sink
 
 
 def h3q_quantize_nvfp4(x, pqs=None, stream=None):

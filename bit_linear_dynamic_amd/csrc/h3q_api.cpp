@@ -710,6 +710,18 @@ h3q_status h3q_adaln_apply(void* stream, const uint16_t* M, const float* bias, c
   return ok();
 }
 
+h3q_status h3q_mfma_loop(void* stream, const uint16_t* ops_a, const uint16_t* ops_b, int32_t iters,
+                         int32_t workgroups, float* sink) {
+  if (!ops_a || !ops_b || !sink) return fail(H3Q_E_ARG, "mfma_loop: null pointer");
+  if (!aligned16(ops_a) || !aligned16(ops_b)) return fail(H3Q_E_ARG, "mfma_loop: operands must be 16-byte aligned");
+  if (iters < 1 || workgroups < 1 || workgroups > (1 << 20)) return fail(H3Q_E_ARG, "mfma_loop: bad iters or workgroups");
+  int dev;
+  if (h3q_status st = check_device(&dev)) return st;
+  hipError_t e = launch_mfma_loop(ops_a, ops_b, iters, workgroups, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(H3Q_E_HIP, "mfma_loop launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 h3q_status h3q_weight_checksum(void* stream, h3q_weight w, uint64_t* out) {
   if (!live(w)) return fail(H3Q_E_ARG, "weight_checksum: not a live weight handle");
   if (!out) return fail(H3Q_E_ARG, "weight_checksum: null output");

@@ -120,6 +120,9 @@ struct DequantParams {
   uint16_t* out;            // bf16 [N][K]
 };
 hipError_t launch_debug_dequant(const DequantParams& p, hipStream_t stream);
+// 64 MFMAs of 32x32x16 per wave and iteration; ops_a, ops_b: bf16 [8][256][8]; sink: [workgroups * 256]
+hipError_t launch_mfma_loop(const uint16_t* ops_a, const uint16_t* ops_b, int32_t iters, int32_t workgroups,
+                            float* sink, hipStream_t stream);
 
 // Merged route (merge.hip): m = f32(Wq * ts + c * (B A) / pqs) in fp64, rows in the caller's order.
 struct MergeParams {

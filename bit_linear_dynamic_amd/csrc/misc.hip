@@ -1,5 +1,6 @@
-// misc.hip -- diagnostic kernel: the packed weight decoded back to the caller's [N][K] order with
-// the decode routine the GEMM uses (E2M1 * E4M3, exact in bf16, without the tensor scale).
+// misc.hip -- diagnostic kernels: the packed weight decoded back to the caller's [N][K] order with
+// the decode routine the GEMM uses (E2M1 * E4M3, exact in bf16, without the tensor scale), and a pure
+// matrix-core loop that measures the MFMA throughput the board sustains.
 #include "h3q_device.hpp"
 #include "h3q_kernels.hpp"
 
@@ -42,7 +43,45 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(DequantParams p) {
   }
 }
 
+// Matrix-core ceiling under the board's power limit: every wave keeps 8 accumulator chains of
+// v_mfma_f32_32x32x16_bf16 busy with 8 operand pairs that rotate every step (so consecutive MFMAs see
+// different data, as in a GEMM), two waves per SIMD as the main GEMM runs, no memory traffic in the
+// loop. The accumulators are summed into `sink` so that nothing is optimized away.
+__global__ __launch_bounds__(256, 2) void mfma_loop_kernel(const u32x4* ops_a, const u32x4* ops_b, int32_t iters,
+                                                          float* sink) {
+  const int tid = threadIdx.x;
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = __builtin_bit_cast(bf16x8, ops_a[j * 256 + tid]);
+    b[j] = __builtin_bit_cast(bf16x8, ops_b[j * 256 + tid]);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[(j + s) & 7], acc[j], 0, 0, 0);
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t += acc[j][e];
+  sink[static_cast<int64_t>(blockIdx.x) * 256 + tid] = t;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_loop(const uint16_t* ops_a, const uint16_t* ops_b, int32_t iters, int32_t workgroups,
+                            float* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(workgroups), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(ops_a),
+                     reinterpret_cast<const u32x4*>(ops_b), iters, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_debug_dequant(const DequantParams& p, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(p.n_tiles) * kGemmBN * p.k_tiles;

@@ -206,6 +206,16 @@ h3q_status h3q_adaln_table(void* stream, const float* u, const float* emb, const
 h3q_status h3q_adaln_apply(void* stream, const uint16_t* M, const float* bias, const float* table, const float* t,
                            int32_t T, int32_t blocks, int64_t rows, int32_t samples, int32_t R, float* out);
 
+/* Measurement aid: the matrix-core throughput the board sustains under its power limit, beside which
+ * the GEMM's rate is read (the nominal dense bf16 peak assumes the full engine clock). Each of the
+ * `workgroups` workgroups of 256 threads (two waves per SIMD, as the main GEMM runs) performs
+ * iters x 64 v_mfma_f32_32x32x16_bf16 per wave (32768 flops each) on 8 rotating operand pairs, with no
+ * memory traffic in the loop: flops = workgroups * 4 * iters * 64 * 32768. Device pointers: ops_a,
+ * ops_b bf16 [8][256][8] (16-byte aligned; the operand values, e.g. activation-like and decoded-weight-
+ * like data), sink fp32 [workgroups * 256] (written, meaningless). Asynchronous on `stream`. */
+h3q_status h3q_mfma_loop(void* stream, const uint16_t* ops_a, const uint16_t* ops_b, int32_t iters,
+                         int32_t workgroups, float* sink);
+
 /* The W4A4 activation quantizer on its own (MiniMax-H3 Ultra Fast, "Kernel path", item 1), as
  * h3q_linear_ex(H3Q_ACT_NVFP4) runs it:
  *   v      = f32(x) * pqs[k] rounded to fp32            (pqs NULL -> v = x)

@@ -574,6 +574,8 @@ h3q_status h3q_linear_swiglu_emit(void* stream, const uint16_t* x, int64_t S, co
     const uintptr_t hb = reinterpret_cast<uintptr_t>(h), he = hb + static_cast<uintptr_t>(S * F * 2);
     const uintptr_t sb = reinterpret_cast<uintptr_t>(xs_next), se = sb + static_cast<uintptr_t>(S * F * 2);
     if (S > 0 && hb < se && sb < he) return fail(H3Q_E_ARG, "swiglu_emit: xs_next overlaps h");
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), xe = xb + static_cast<uintptr_t>(S * w->K * 2);
+    if (S > 0 && xb < se && sb < xe) return fail(H3Q_E_ARG, "swiglu_emit: xs_next overlaps x");
   }
   const FuseArgs fa{pqs_next, xs_next, nullptr};
   return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags | H3Q_EPI_SWIGLU, h, nullptr, &fa);

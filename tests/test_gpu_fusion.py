@@ -153,6 +153,15 @@ def test_fusion_argument_errors():
         expect(h3q.H3Q_E_SHAPE, lambda: h3q.h3q_linear_swiglu_emit(x, None, gu.handle, NONE, 0.0, pq))
         expect(h3q.H3Q_E_ARG, lambda: h3q.h3q_linear_swiglu_emit(x, None, plain.handle, NONE, 0.0,
                                                                   torch.ones(32, device="cuda")))
+        gu16 = Proj(2 * 32, 64, 1805, gate_up=True)
+        try:
+            big = torch.zeros(8 * 64 + 64, dtype=torch.bfloat16, device="cuda")
+            xo = big[:8 * 64].view(8, 64)
+            expect(h3q.H3Q_E_ARG, lambda: h3q.h3q_linear_swiglu_emit(xo, None, gu16.handle, NONE, 0.0,
+                                                                      torch.ones(32, device="cuda"),
+                                                                      xs_next=big[64:64 + 8 * 32].view(8, 32)))
+        finally:
+            gu16.free()
         x80 = synth.activation(8, 80, 1804).cuda()
         expect(h3q.H3Q_E_SHAPE, lambda: h3q.h3q_linear_prescaled(x80, x80.clone(), odd_k.handle, NONE, 0.0))
         buf = torch.zeros(8 * 64 + 8, dtype=torch.bfloat16, device="cuda")

@@ -274,6 +274,65 @@ def w4a4_gate_up(projs, stream, calls=5):
             "act_quant_GBps": round(q_bytes / (q * 1e-3) / 1e9, 1), "lora_down_ms": round(l, 4)}
 
 
+def small_s_graph(device, calls=20, replays=10):
+    """The small case (one fused-QKV-like projection 3072 x 1024, rank = alpha = 384, S = 256) is
+    launch-bound: per-call time issued eagerly against the same calls captured once into a HIP graph
+    and replayed (after one eager call has sized the stream's workspace)."""
+    import torch
+
+    import bit_linear_dynamic_amd as h3q
+    from bit_linear_dynamic_amd import synth
+    from bit_linear_dynamic_amd import workloads as wl
+
+    p, S = wl.SMALL_QKV, wl.S_SMALL
+    w = synth.weight_fp32(p.N, p.K, synth.seed_of(1, 0, synth.W), device).to(torch.bfloat16)
+    codes, scales, ts = h3q.h3q_quantize_nvfp4(w)
+    torch.cuda.synchronize()
+    handle = h3q.h3q_pack_weight(codes.cpu(), scales.cpu(), ts.item(), p.N, p.K)
+    try:
+        A, B = synth.lora_factors(p.N, p.K, p.rank, synth.seed_of(1, 0, synth.A1), synth.seed_of(1, 0, synth.B1))
+        h3q.h3q_register_adapter(handle, 1, A, B, p.rank, p.alpha)
+        x = synth.activation(S, p.K, synth.seed_of(1, 0, synth.X), device)
+        pqs = synth.pre_quant_scale(p.K, synth.seed_of(1, 0, synth.PQS), device)
+        y = torch.empty((S, p.N), dtype=torch.bfloat16, device=device)
+        s = torch.cuda.Stream()
+
+        def run():
+            for _ in range(calls):
+                h3q.h3q_linear(x, pqs, handle, 1, 1.0, y=y, stream=s)
+
+        with torch.cuda.stream(s):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            a.record(s)
+            for _ in range(replays):
+                run()
+            b.record(s)
+        torch.cuda.synchronize()
+        eager_us = a.elapsed_time(b) * 1e3 / (calls * replays)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+            a.record(s)
+            for _ in range(replays):
+                g.replay()
+            b.record(s)
+        torch.cuda.synchronize()
+        graph_us = a.elapsed_time(b) * 1e3 / (calls * replays)
+        flops = wl.effective_flops(S, p)
+        return {"projection": [p.N, p.K, p.rank], "S": S, "eager_us_per_call": round(eager_us, 2),
+                "graph_us_per_call": round(graph_us, 2), "graph_tflops": round(flops / (graph_us * 1e-6) / 1e12, 1),
+                "eager_tflops": round(flops / (eager_us * 1e-6) / 1e12, 1)}
+    finally:
+        torch.cuda.synchronize()
+        h3q.h3q_free_weight(handle)
+
+
 def mfma_ceiling(stream, device, gemm_achieved):
     """The matrix-core rate the board sustains under its power limit (h3q_mfma_loop: rotating operand
     pairs, two waves per SIMD, no memory traffic), on activation-like bf16 N(0, 1) operands against
@@ -444,6 +503,7 @@ def main():
     fusion = None if args.timed_only else producer_fusion(projs, stream)
     w4a4 = None if args.timed_only else w4a4_gate_up(projs, stream)
     ceiling = None if args.timed_only else mfma_ceiling(stream, device, achieved)
+    small = None if args.timed_only else small_s_graph(device)
 
     cpu = None
     if not args.no_cpu:
@@ -482,6 +542,7 @@ def main():
         "mlp_producer_fusion": fusion,
         "w4a4_swiglu_gate_up": w4a4,
         "mfma_loop_ceiling": ceiling,
+        "small_s_latency": small,
         "cpu_baseline": cpu,
     }
     for d in projs:

@@ -160,22 +160,40 @@ hipError_t timed(int kind, hipStream_t stream, F&& fn) {
 }
 
 // ---- per-(device, stream) grow-only workspace ----
+// Under stream capture a call bakes the workspace's address into the graph, so a buffer that a
+// capture has seen is never freed: when it must grow later, it is retired (kept until the process
+// ends) and a new one is allocated. Growing it during a capture is refused (the allocation and the
+// synchronization it needs cannot be captured): run the call once outside the capture first, on the
+// same stream, with the same or a larger S.
 struct Workspace {
   void* buf = nullptr;
   size_t bytes = 0;
+  bool captured = false;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<void*> g_ws_retired;
 
 h3q_status workspace(int dev, hipStream_t stream, size_t need, uint8_t** out) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace& ws = g_ws[{dev, stream}];
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  H3Q_HIP_TRY(hipStreamIsCapturing(stream, &cs));
+  const bool capturing = cs != hipStreamCaptureStatusNone;
   if (ws.bytes < need) {
+    if (capturing)
+      return fail(H3Q_E_ARG, "workspace of %zu bytes needed during stream capture (have %zu): make the same call once "
+                  "outside the capture on this stream first", need, ws.bytes);
     if (ws.buf) {
       H3Q_HIP_TRY(hipStreamSynchronize(stream));  // in-flight work may still read the old buffer
-      H3Q_HIP_TRY(hipFree(ws.buf));
+      if (ws.captured) {
+        g_ws_retired.push_back(ws.buf);  // a captured graph may still use it
+      } else {
+        H3Q_HIP_TRY(hipFree(ws.buf));
+      }
       ws.buf = nullptr;
       ws.bytes = 0;
+      ws.captured = false;
     }
     const size_t bytes = static_cast<size_t>(round_up(static_cast<int64_t>(need), int64_t{1} << 21));
     if (dev_alloc(&ws.buf, bytes) != hipSuccess) {
@@ -185,6 +203,7 @@ h3q_status workspace(int dev, hipStream_t stream, size_t need, uint8_t** out) {
     }
     ws.bytes = bytes;
   }
+  if (capturing) ws.captured = true;
   *out = static_cast<uint8_t*>(ws.buf);
   return H3Q_OK;
 }

@@ -28,6 +28,14 @@
  *     must be made with that device current.
  *   - calls on different streams may run concurrently; registering or unregistering an adapter
  *     while a call that uses the same handle is in flight is not allowed.
+ *   - the linear entry points use a device workspace per (device, stream), grown when a call needs
+ *     more (t', the prescaled or quantized activation); growing synchronizes that stream.
+ *   - stream capture (HIP graphs): the linear entry points may be captured once the same call (same
+ *     or larger S) has run on the capturing stream outside the capture, so that its workspace is
+ *     sized; a capture that would need a larger workspace fails with H3Q_E_ARG. A workspace a
+ *     capture has used is never freed (if it must grow later, it is retired until the process ends),
+ *     so graphs stay valid. Timing (h3q_timing_enable) must be off while capturing. Pack, register,
+ *     merge, checksum and the AdaLN table build are not meant for capture.
  */
 #ifndef H3Q_H
 #define H3Q_H

@@ -201,6 +201,9 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
 #pragma unroll
   for (int t = 0; t < L; ++t) issue_tile<RTM, NC>(c, t, smem0 + t * G::kStage);
   int s_cur = 0;
+  // Not unrolled: unrolled by the stage count, some shapes had their accumulators moved between
+  // AGPRs and VGPRs hundreds of times per tile and ran at a third of the copy rate.
+#pragma unroll 1
   for (int kt = 0; kt < c.k_tiles; ++kt) {
     wait_tile<L, CPT, NS>(kt);
     const int s_iss = s_cur == 0 ? NST - 1 : s_cur - 1;  // (kt + L) % NST: the stage of tile kt - 1
@@ -208,6 +211,9 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
     const uint8_t* st = smem + s_cur * G::kStage;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
+      // Column tile jt = wave + 4j is always inside the stage's A area (CT = 4 NC tiles); a tile at or
+      // past ct holds no copy of A, and its accumulator is computed but never stored. No branch: with
+      // one, the compiler moved the accumulators between AGPRs and VGPRs around every MFMA.
       bf16x8 a[RTM], b[NC];
 #pragma unroll
       for (int i = 0; i < RTM; ++i)
@@ -215,15 +221,13 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int jt = static_cast<int>(wave) + 4 * j;
-        b[j] = jt < ct ? *reinterpret_cast<const bf16x8*>(st + G::kA + tile_offset<BK>(jt * 32 + r32, kk * 2 + h32))
-                       : bf16x8{};
+        b[j] = *reinterpret_cast<const bf16x8*>(st + G::kA + tile_offset<BK>(jt * 32 + r32, kk * 2 + h32));
       }
 #pragma unroll
       for (int i = 0; i < RTM; ++i)
 #pragma unroll
         for (int j = 0; j < NC; ++j)
-          if (static_cast<int>(wave) + 4 * j < ct)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     if (XS) {
       // xs = bf16(x * pqs) of the whole tile from its LDS copy, row-major: chunk q of the workgroup

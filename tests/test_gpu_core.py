@@ -186,7 +186,9 @@ def test_store_paths_agree(N, gate_up):
 
 @pytest.mark.parametrize("S,K,N,rank,alpha,strength", [(256, 1024, 3072, 384, 384.0, 1.0),
                                                        (37, 208, 300, 65, 16.0, -1.5),
-                                                       (300, 6144, 520, 128, 32.0, 0.5)])
+                                                       (300, 6144, 520, 128, 32.0, 0.5),
+                                                       (70, 320, 400, 150, 75.0, 1.0),
+                                                       (48, 256, 260, 300, 64.0, 0.75)])
 def test_mirror_tight_parity(S, K, N, rank, alpha, strength):
     """Against the mirror oracle (exact arithmetic with the GPU's declared rounding points: xs and t' in
     bf16, one fp32 scale, bf16 store) the only difference left is the GPU's fp32 accumulation, which

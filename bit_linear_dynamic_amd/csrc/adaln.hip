@@ -8,8 +8,10 @@
 //
 // adaln_table_kernel: one wave per 4 samples of one block; lanes split the E-wide dot products
 //   A_b[j] . silu(e_i) (fp32, silu(z) = z / (1 + exp(-z))) in 8-column chunks, then a butterfly
-//   reduction. A one-off per adapter and strength: 2 * blocks * S * rl * E flops (4.4 GFLOP for 50
-//   blocks of rank 16).
+//   reduction. The block is the fast grid index, so the workgroups of one group of 16 samples run
+//   together and read those embedding rows from L2 instead of streaming e once per block. A
+//   one-off per adapter and strength: 2 * blocks * S * rl * E flops (4.4 GFLOP for 50 blocks of
+//   rank 16).
 // adaln_apply_kernel: a stream over [W_p | B] (bf16 [rows][R] per block, R = rb + rl): one row per
 //   thread, R / 8 16-byte loads, T outputs per row from the T interpolated v's kept in LDS. Bytes per
 //   call: blocks * rows * (2 R + 4 [bias] + 4 T [out]) -- HBM-bound.
@@ -24,7 +26,7 @@ constexpr int kMaxRl = 32;
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
-constexpr int kSamplesPerWave = 4;
+constexpr int kSamplesPerWave = 4;  // 16 per workgroup: grid y = ceil(S / 16) <= 65535
 
 // 8 consecutive values of one embedding row through silu (zeros past E).
 __device__ __forceinline__ void silu8(const float* row, int E, int k0, float (&s)[8]) {
@@ -62,8 +64,8 @@ __device__ __forceinline__ void a8(const uint16_t* row, int E, int k0, float (&a
 __global__ __launch_bounds__(256) void adaln_table_kernel(AdalnTableParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  const int i0 = (blockIdx.x * 4 + wave) * kSamplesPerWave;
+  const int b = blockIdx.x;
+  const int i0 = (blockIdx.y * 4 + wave) * kSamplesPerWave;
   if (i0 >= p.S) return;
   const int ns = min(kSamplesPerWave, p.S - i0);
   const int R = p.rb + p.rl;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kApplyThreads) void adaln_apply_kernel(AdalnApplyPa
 
 hipError_t launch_adaln_table(const AdalnTableParams& p, hipStream_t stream) {
   const int per_wg = 4 * kSamplesPerWave;
-  const dim3 grid(static_cast<uint32_t>((p.S + per_wg - 1) / per_wg), static_cast<uint32_t>(p.blocks));
+  const dim3 grid(static_cast<uint32_t>(p.blocks), static_cast<uint32_t>((p.S + per_wg - 1) / per_wg));
   hipLaunchKernelGGL(adaln_table_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -703,10 +703,10 @@ h3q_status h3q_adaln_table(void* stream, const float* u, const float* emb, const
                            int32_t blocks, int32_t samples, int32_t emb_dim, int32_t base_rank, int32_t lora_rank,
                            float* table) {
   if (!u || !emb || !table || (lora_rank > 0 && !A)) return fail(H3Q_E_ARG, "adaln_table: null pointer");
-  if (blocks < 1 || blocks > 65535 || samples < 2 || emb_dim < 1 || base_rank < 1 || base_rank > 64 || lora_rank < 0 || lora_rank > 32 ||
-      base_rank + lora_rank > 64 || static_cast<int64_t>(samples) * emb_dim > (int64_t{1} << 31))
-    return fail(H3Q_E_SHAPE, "adaln_table: need blocks >= 1, samples >= 2, emb_dim >= 1, 1 <= base_rank, 0 <= lora_rank <= 32, "
-                "base_rank + lora_rank <= 64");
+  if (blocks < 1 || blocks > 65535 || samples < 2 || samples > 65535 * 16 || emb_dim < 1 || base_rank < 1 || base_rank > 64 ||
+      lora_rank < 0 || lora_rank > 32 || base_rank + lora_rank > 64 || static_cast<int64_t>(samples) * emb_dim > (int64_t{1} << 31))
+    return fail(H3Q_E_SHAPE, "adaln_table: need 1 <= blocks <= 65535, 2 <= samples <= 1048560, emb_dim >= 1, 1 <= base_rank, "
+                "0 <= lora_rank <= 32, base_rank + lora_rank <= 64");
   if (!std::isfinite(scale)) return fail(H3Q_E_ARG, "adaln_table: scale must be finite");
   int dev;
   if (h3q_status st = check_device(&dev)) return st;

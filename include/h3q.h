@@ -198,7 +198,8 @@ h3q_status h3q_merge_adapter(void* stream, h3q_weight w, int32_t adapter_id, flo
  *   emb    fp32 [samples][emb_dim]          (the timestep embedding at the sample points)
  *   A      bf16 [blocks][lora_rank][emb_dim] (NULL if lora_rank is 0)
  *   table  fp32 [blocks][samples][base_rank + lora_rank]
- * 1 <= blocks <= 65535, samples >= 2, 1 <= base_rank, 0 <= lora_rank <= 32, base_rank + lora_rank <= 64.
+ * 1 <= blocks <= 65535, 2 <= samples <= 1048560, 1 <= base_rank, 0 <= lora_rank <= 32,
+ * base_rank + lora_rank <= 64, samples * emb_dim <= 2^31.
  * Asynchronous.
  *
  * h3q_adaln_apply: for each of the T requested times (clamped to [0, 1]), with p = t (samples - 1),

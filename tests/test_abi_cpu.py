@@ -159,7 +159,8 @@ def test_side_entry_points_reject_bad_arguments(lib):
     assert lib.h3q_adaln_table(None, None, f, p, 1.0, 1, 5, 8, 8, 16, f) == h3q.H3Q_E_ARG
     assert lib.h3q_adaln_table(None, f, f, None, 1.0, 1, 5, 8, 8, 16, f) == h3q.H3Q_E_ARG   # A needed for lora_rank > 0
     for blocks, samples, emb, rb, rl in ((0, 5, 8, 8, 16), (1, 1, 8, 8, 16), (1, 5, 0, 8, 16), (1, 5, 8, 0, 16),
-                                         (1, 5, 8, 8, 33), (1, 5, 8, 40, 32), (70000, 5, 8, 8, 16)):
+                                         (1, 5, 8, 8, 33), (1, 5, 8, 40, 32), (70000, 5, 8, 8, 16),
+                                         (1, 65535 * 16 + 1, 8, 8, 16)):
         assert lib.h3q_adaln_table(None, f, f, p, 1.0, blocks, samples, emb, rb, rl, f) == h3q.H3Q_E_SHAPE, \
             (blocks, samples, emb, rb, rl)
     assert lib.h3q_adaln_table(None, f, f, p, math.inf, 1, 5, 8, 8, 16, f) == h3q.H3Q_E_ARG

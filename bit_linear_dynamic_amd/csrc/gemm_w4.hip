@@ -11,15 +11,17 @@
 // with t' = strength*alpha/(rank*ts) * (A x) so that one scale by ts finishes both terms. The gate/up
 // epilogue is the in-place SiLU x up of MiniMax-H3 Ultra Fast, "Kernel path".
 //
-// Geometry: 256 threads = 4 wave64s side by side (1 x 4), a 128 x 256 output tile per workgroup;
-// wave w owns all 128 rows and columns [64w, 64w+64) as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
-// with fp32 accumulators (128 AGPRs). Two workgroups share a CU, so every SIMD runs two waves: the
-// matrix core works on one wave's MFMAs while the other issues its decode, LDS reads and copies.
-// K is staged through three LDS stages of 26 KiB, two tiles ahead:
-//   base K-tile (64 deep)  activation 128 x 64 bf16, 16-byte chunks XOR-swizzled     16 KiB
+// Geometry: 256 threads = 4 wave64s side by side (1 x 4), a 256 x 256 output tile per workgroup;
+// wave w owns all 256 rows and columns [64w, 64w+64) as 8 x 2 tiles of v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators (256 AGPRs), so one workgroup fills a CU and each SIMD runs one wave that
+// issues its own decode, LDS reads and copies between its MFMAs. Every decoded weight value feeds
+// eight MFMAs (256 rows), which halves the decode and copy work per flop against a 128-row tile;
+// under the board's power limit that work is paid for in clock. K is staged through three LDS
+// stages of 42 KiB, two tiles ahead:
+//   base K-tile (64 deep)  activation 256 x 64 bf16, 16-byte chunks XOR-swizzled     32 KiB
 //                          8 runs of 256 code dwords (+32 dwords padding each)        9 KiB
 //                          256 scale dwords                                            1 KiB
-//   LoRA K-tile (32 deep)  t' 128 x 32 bf16 (8 KiB) and B 256 x 32 bf16 (16 KiB), same swizzle
+//   LoRA K-tile (32 deep)  t' 256 x 32 bf16 (16 KiB) and B 256 x 32 bf16 (16 KiB), same swizzle
 // Every global->LDS copy is a buffer_load ... lds (16 bytes per lane, no registers, out-of-range
 // offsets read as zero). The weight stays 4-bit in LDS: each wave decodes the B operand of its own 64
 // columns straight into MFMA registers -- one code dword (8 consecutive k of one column) and one
@@ -44,19 +46,22 @@ constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
 constexpr int kThreads = 256;
 constexpr uint32_t kCodeRun = (kGemmBN + 32) * 4;        // one code run in LDS, padded: 1152 B
 constexpr uint32_t kLdsA = 0;                            // activation / t' tile
-constexpr uint32_t kLdsCodes = BM * BK * 2;              // base tile: code runs (16384)
-constexpr uint32_t kLdsScales = kLdsCodes + kCodeChunksPerTile * kCodeRun;  // 25600
-constexpr uint32_t kLdsLoraB = BM * kLoraBK * 2;         // LoRA tile: B after the 8 KiB t' tile
-constexpr uint32_t kStage = kLdsScales + kScaleTileBytes; // 26624
+constexpr int RT = BM / 32;  // row tiles per wave
+constexpr uint32_t kLdsCodes = BM * BK * 2;              // base tile: code runs (32768)
+constexpr uint32_t kLdsScales = kLdsCodes + kCodeChunksPerTile * kCodeRun;  // 41984
+constexpr uint32_t kLdsLoraB = BM * kLoraBK * 2;         // LoRA tile: B after the 16 KiB t' tile
+constexpr uint32_t kStage = kLdsScales + kScaleTileBytes; // 43008
 constexpr int kStages = 3;
-constexpr int kGroupM = 4;  // row tiles per group in the work order
-constexpr uint32_t kLdsBytes = kStages * kStage;         // 79872: two workgroups per CU
-static_assert(kLdsLoraB + kLoraTileBytes <= kLdsScales, "LoRA tile must leave the scale area free");
-static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups must fit a CU's LDS");
-// DMA instructions per wave per K-tile (every wave issues the same number, so that a wave can wait
-// for all but the newest tile with one vmcnt)
-constexpr int kCopiesBase = 4 + 2 + 1;  // activation, codes, a quarter of the scales
-constexpr int kCopiesLora = 2 + 4;      // t', B
+constexpr int kGroupM = 2;  // row tiles per group in the work order
+// The plain output staging (bf16 [256][264], below) is larger than the three stages.
+constexpr int kOutPitch = 264;
+constexpr uint32_t kLdsBytes = kStages * kStage > BM * kOutPitch * 2 ? kStages * kStage : BM * kOutPitch * 2;
+static_assert(kLdsLoraB + kLoraTileBytes <= kLdsCodes, "LoRA tile must leave the code and scale areas free");
+static_assert(kLdsBytes <= 160 * 1024, "the workgroup must fit a CU's LDS");
+// DMA instructions per wave per copy window (every window issues the same number, so that a wave can
+// wait for all but the newest tile with one vmcnt): 8 of activation (LoRA: 4 of t', 4 of B), 2 code
+// runs, 1 of scales
+constexpr int kCopies = 8 + 2 + 1;
 
 __device__ __forceinline__ u32x4 rsrc(const void* base, uint32_t bytes) { return buf_rsrc(base, bytes); }
 
@@ -69,12 +74,12 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 
 struct Ctx {
   u32x4 act, lt, codes, scales, lb;
-  // Base tile: copy i (of 4 per wave) fills LDS slots (4w + i)*64 + lane, i.e. tile rows
-  // (4w + i)*8 + lane/8; the chunk depends on i only through i & 1, so the per-lane offset is
+  // Base tile: copy i (of 8 per wave) fills LDS slots (8w + i)*64 + lane, i.e. tile rows
+  // (8w + i)*8 + lane/8; the chunk depends on i only through i & 1, so the per-lane offset is
   // vact[i & 1] plus a uniform (i & ~1) * 8 rows.
-  // LoRA tile: t' copy i (of 2 per wave) fills slots (2w + i)*64 + lane of a 64-byte-row tile, i.e.
-  // 128-byte lines (2w + i)*8 + lane/8 holding 16 rows (vlt[i]); B copy i (of 4) fills lines
-  // (4w + i)*8 + lane/8, per-lane part vlb[i & 1], and (i & ~1) adds 16 rows per unit.
+  // LoRA tile: t' copy i (of 4 per wave) fills slots (4w + i)*64 + lane of a 64-byte-row tile, i.e.
+  // 128-byte lines (4w + i)*8 + lane/8 holding 16 rows, per-lane part vlt[i & 1], and (i & ~1) adds
+  // 16 rows per unit; B copy i (of 4) fills lines (4w + i)*8 + lane/8 the same way (vlb[i & 1]).
   uint32_t vact[2], vlt[2], vlb[2];
   uint32_t lane16;  // lane * 16
   uint32_t act_rows8, lt_rows16;
@@ -82,19 +87,22 @@ struct Ctx {
 };
 
 // Copies are issued in windows: the copies of K-tile T are spread over the K-steps between the
-// handover that frees T's stage (that of tile T - 3) and the next handover. A window has 7 copy
-// slots per wave when it spans the four K-steps of a base tile and 6 when it spans two LoRA K-steps:
-//   base tile   slots 0..3 activation (two per 16-row pair), 4 and 5 the two code runs of this
-//               wave's 64 columns, 6 this wave's 256 bytes of block scales (lanes 0..15)
-//   LoRA tile   slots 0 and 1 t', 2..5 B (two per 16-row pair), 6 (in a 7-slot window) a re-read
-// A LoRA tile's slot 6, and every slot of a window past the last tile, re-read the last base tile's
-// scales (or whole tile) into parts of the stage that nothing reads any more, so every window issues
-// the same number of copies and a handover waits with one vmcnt.
+// handover that frees T's stage (that of tile T - 3) and the next handover. A window has 11 copy
+// slots per wave:
+//   base tile   slots 0..7 activation (two per 16-row pair), 8 and 9 the two code runs of this
+//               wave's 64 columns, 10 this wave's 256 bytes of block scales (lanes 0..15)
+//   LoRA tile   slots 0..3 t', 4..7 B (two per 32-row pair of each), 8..10 re-reads of the last
+//               base tile's code runs and scales into the code and scale areas, which LoRA steps
+//               never read
+// Every slot of a window past the last tile re-reads the last base tile into the stage just left,
+// so every window issues the same number of copies and a handover waits with one vmcnt.
 struct Win {
-  uint32_t g01, g23, g4, g5, g6;  // LDS addresses: slots 0/1 and 2/3 (+1 KiB for the odd one), 4, 5, 6
-  uint32_t s01, s23, s4, s5, s6;  // uniform offsets
-  u32x4 r01, r23, r45;            // descriptors (slot 6: the scales)
-  uint32_t v0, v1, v2, v3, v4, v5;  // per-lane offsets
+  uint32_t gA, gB, gC, gS;     // LDS: slots 0..3 at gA + i KiB, 4..7 at gB + (i - 4) KiB, 8 and 9 at
+                               // gC and gC + 4 code runs, 10 at gS
+  uint32_t s0, s2, s4, s6;     // uniform offsets of slot pairs (0, 1), (2, 3), (4, 5), (6, 7)
+  uint32_t sC, sS;             // uniform offsets of slot 8 (slot 9: + 4 KiB) and slot 10
+  u32x4 rA, rB;                // descriptors of slots 0..3 and 4..7
+  uint32_t v0, v1, v4, v5;     // per-lane offsets: slots 0..3 alternate v0 / v1, slots 4..7 v4 / v5
 };
 
 template <bool LORA>
@@ -102,71 +110,63 @@ __device__ __forceinline__ Win plan(const Ctx& c, int T, uint32_t stage) {
   Win w;
   const uint32_t wv = static_cast<uint32_t>(c.wave);
   const uint32_t kb = static_cast<uint32_t>(T < c.k_tiles ? T : c.k_tiles - 1);
-  w.g6 = stage + kLdsScales + wv * 256;
-  w.s6 = kb * kScaleTileBytes + wv * 256;
+  // code runs and scales of base tile kb (for a LoRA tile: of the last base tile, into areas that
+  // LoRA steps do not read)
+  w.gC = stage + kLdsCodes + wv * kCodeRun;
+  w.gS = stage + kLdsScales + wv * 256;
+  w.sC = kb * kCodeTileBytes + wv * 1024;
+  w.sS = kb * kScaleTileBytes + wv * 256;
   if (!LORA || T < c.k_tiles || T >= c.total) {  // base tile kb (a harmless re-read past the end)
     const uint32_t k_bytes = kb * BK * 2;
-    w.g01 = stage + kLdsA + wv * 4096;
-    w.g23 = w.g01 + 2048;
-    w.g4 = stage + kLdsCodes + wv * kCodeRun;
-    w.g5 = w.g4 + 4 * kCodeRun;
-    w.s01 = k_bytes;
-    w.s23 = k_bytes + 2 * c.act_rows8;
-    w.s4 = kb * kCodeTileBytes + wv * 1024;
-    w.s5 = w.s4 + 4 * 1024;
-    w.r01 = c.act;
-    w.r23 = c.act;
-    w.r45 = c.codes;
-    w.v0 = c.vact[0]; w.v1 = c.vact[1]; w.v2 = c.vact[0]; w.v3 = c.vact[1];
-    w.v4 = c.lane16; w.v5 = c.lane16;
+    w.gA = stage + kLdsA + wv * 8192;
+    w.gB = w.gA + 4096;
+    w.s0 = k_bytes;
+    w.s2 = k_bytes + 2 * c.act_rows8;
+    w.s4 = k_bytes + 4 * c.act_rows8;
+    w.s6 = k_bytes + 6 * c.act_rows8;
+    w.rA = c.act;
+    w.rB = c.act;
+    w.v0 = c.vact[0]; w.v1 = c.vact[1]; w.v4 = c.vact[0]; w.v5 = c.vact[1];
   } else {  // LoRA tile rt: t' then B
     const uint32_t rt = static_cast<uint32_t>(T - c.k_tiles);
-    w.g01 = stage + kLdsA + wv * 2048;
-    w.g23 = stage + kLdsLoraB + wv * 4096;
-    w.g4 = w.g23 + 2048;
-    w.g5 = w.g23 + 3072;
-    w.s01 = rt * kLoraBK * 2;
-    w.s23 = rt * kLoraTileBytes;
-    w.s4 = w.s23 + 2 * (16 * kLoraBK * 2);
-    w.s5 = w.s4;
-    w.r01 = c.lt;
-    w.r23 = c.lb;
-    w.r45 = c.lb;
-    w.v0 = c.vlt[0]; w.v1 = c.vlt[1]; w.v2 = c.vlb[0]; w.v3 = c.vlb[1];
-    w.v4 = c.vlb[0]; w.v5 = c.vlb[1];
+    w.gA = stage + kLdsA + wv * 4096;
+    w.gB = stage + kLdsLoraB + wv * 4096;
+    w.s0 = rt * kLoraBK * 2;
+    w.s2 = w.s0 + 2 * c.lt_rows16;
+    w.s4 = rt * kLoraTileBytes;
+    w.s6 = w.s4 + 2 * (16 * kLoraBK * 2);
+    w.rA = c.lt;
+    w.rB = c.lb;
+    w.v0 = c.vlt[0]; w.v1 = c.vlt[1]; w.v4 = c.vlb[0]; w.v5 = c.vlb[1];
   }
   return w;
 }
 
 template <int I> __device__ __forceinline__ uint32_t slot_m0(const Win& w) {
-  if constexpr (I == 0) return w.g01;
-  else if constexpr (I == 1) return w.g01 + 1024;
-  else if constexpr (I == 2) return w.g23;
-  else if constexpr (I == 3) return w.g23 + 1024;
-  else if constexpr (I == 4) return w.g4;
-  else if constexpr (I == 5) return w.g5;
-  else return w.g6;
+  if constexpr (I < 4) return w.gA + I * 1024;
+  else if constexpr (I < 8) return w.gB + (I - 4) * 1024;
+  else if constexpr (I == 8) return w.gC;
+  else if constexpr (I == 9) return w.gC + 4 * kCodeRun;
+  else return w.gS;
 }
 template <int I> __device__ __forceinline__ uint32_t slot_soff(const Win& w) {
-  if constexpr (I < 2) return w.s01;
-  else if constexpr (I < 4) return w.s23;
-  else if constexpr (I == 4) return w.s4;
-  else if constexpr (I == 5) return w.s5;
-  else return w.s6;
+  if constexpr (I < 2) return w.s0;
+  else if constexpr (I < 4) return w.s2;
+  else if constexpr (I < 6) return w.s4;
+  else if constexpr (I < 8) return w.s6;
+  else if constexpr (I == 8) return w.sC;
+  else if constexpr (I == 9) return w.sC + 4 * 1024;
+  else return w.sS;
 }
 template <int I> __device__ __forceinline__ uint32_t slot_voff(const Ctx& c, const Win& w) {
-  if constexpr (I == 0) return w.v0;
-  else if constexpr (I == 1) return w.v1;
-  else if constexpr (I == 2) return w.v2;
-  else if constexpr (I == 3) return w.v3;
-  else if constexpr (I == 4) return w.v4;
-  else if constexpr (I == 5) return w.v5;
+  if constexpr (I < 4) return (I & 1) ? w.v1 : w.v0;
+  else if constexpr (I < 8) return (I & 1) ? w.v5 : w.v4;
   else return c.lane16;
 }
 template <int I> __device__ __forceinline__ u32x4 slot_rsrc(const Ctx& c, const Win& w) {
-  if constexpr (I < 2) return w.r01;
-  else if constexpr (I < 4) return w.r23;
-  else if constexpr (I < 6) return w.r45;
+  if constexpr (I < 4) return w.rA;
+  else if constexpr (I < 8) return w.rB;
+  else if constexpr (I < 10) return c.codes;
   else return c.scales;
 }
 
@@ -179,7 +179,7 @@ template <int I> __device__ __forceinline__ u32x4 slot_rsrc(const Ctx& c, const 
 template <int I>
 __device__ __forceinline__ void copy_slot(const Ctx& c, const Win& w) {
   uint32_t msv;
-  if constexpr (I == 6) {
+  if constexpr (I == 10) {
     uint64_t ex;
     asm volatile(
         "s_mov_b32 %[msv], m0\n\ts_mov_b64 %[ex], exec\n\ts_mov_b32 exec_lo, 0xffff\n\ts_mov_b32 exec_hi, 0\n\t"
@@ -214,9 +214,15 @@ __device__ __forceinline__ void copy_slots(const Ctx& c, const Win& w) {
 
 #define H3Q_ACC(acc)                                                                            \
   [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]),   \
-  [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1])
-#define H3Q_A_IN(a) [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3])
-#define H3Q_A_OUT(n) [n0] "=&v"(n[0]), [n1] "=&v"(n[1]), [n2] "=&v"(n[2]), [n3] "=&v"(n[3])
+  [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]),   \
+  [c40] "+a"(acc[4][0]), [c41] "+a"(acc[4][1]), [c50] "+a"(acc[5][0]), [c51] "+a"(acc[5][1]),   \
+  [c60] "+a"(acc[6][0]), [c61] "+a"(acc[6][1]), [c70] "+a"(acc[7][0]), [c71] "+a"(acc[7][1])
+#define H3Q_A_IN(a)                                                                             \
+  [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [a4] "v"(a[4]), [a5] "v"(a[5]), \
+  [a6] "v"(a[6]), [a7] "v"(a[7])
+#define H3Q_A_OUT(n)                                                                            \
+  [n0] "=&v"(n[0]), [n1] "=&v"(n[1]), [n2] "=&v"(n[2]), [n3] "=&v"(n[3]), [n4] "=&v"(n[4]),    \
+  [n5] "=&v"(n[5]), [n6] "=&v"(n[6]), [n7] "=&v"(n[7])
 #define H3Q_B_IN(b)                                                                             \
   [bq0] "v"(u32x4{b[0], b[1], b[2], b[3]}), [bq1] "v"(u32x4{b[4], b[5], b[6], b[7]})
 #define H3Q_B_OUT(m)                                                                            \
@@ -224,50 +230,51 @@ __device__ __forceinline__ void copy_slots(const Ctx& c, const Win& w) {
   [m5] "=&v"(m[5]), [m6] "=&v"(m[6]), [m7] "=&v"(m[7])
 #define H3Q_STEP_CLOBBERS                                                                       \
   "v108", "v109", "v110", "v111", "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127", "memory"
+static_assert(RT == 8, "the step blocks and the operand lists above are written for 8 row tiles");
 
 typedef uint32_t bw_t[8];  // a decoded W4 B operand: 2 column tiles x 4 dwords of bf16 pairs
+typedef f32x16 acc_t[RT][2];
+typedef bf16x8 aop_t[RT];
 
 constexpr uint32_t kPermHighHalves = 0x07060302u;  // v_perm_b32: high 16 bits of each source
 
-// base step, next = K-step of the same base tile (scales s0/s1 of that step given); copies I, I+1
+// base step, next = K-step of the same base tile (scales s0/s1 of that step given); copies I..I+2
 template <int I>
-__device__ __forceinline__ void step_bb2(f32x16 (&acc)[4][2], const bf16x8 (&a)[4], const bw_t& b, bf16x8 (&n)[4],
-                                         bw_t& m, float s0, float s1, uint32_t aaddr, uint32_t caddr, const Ctx& c,
-                                         const Win& w) {
+__device__ __forceinline__ void step_bb3(acc_t& acc, const aop_t& a, const bw_t& b, aop_t& n, bw_t& m, float s0,
+                                         float s1, uint32_t aaddr, uint32_t caddr, const Ctx& c, const Win& w) {
   uint32_t msv;
-  asm volatile(H3Q_STEP_BB_C2_ASM
+  asm volatile(H3Q_STEP_BB_C3_ASM
                : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [msv] "=&s"(msv)
                : H3Q_A_IN(a), H3Q_B_IN(b), [s0] "v"(s0), [s1] "v"(s1), [aaddr] "v"(aaddr), [caddr] "v"(caddr),
-                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, I), H3Q_COPY(1, I + 1)
+                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, I), H3Q_COPY(1, I + 1), H3Q_COPY(2, I + 2)
                : H3Q_STEP_CLOBBERS);
 }
-// the same with copy 6 (the scales, lanes 0..15)
-__device__ __forceinline__ void step_bbm(f32x16 (&acc)[4][2], const bf16x8 (&a)[4], const bw_t& b, bf16x8 (&n)[4],
-                                          bw_t& m, float s0, float s1, uint32_t aaddr, uint32_t caddr, const Ctx& c,
-                                          const Win& w) {
+// the same with copies 9 and 10 (the scales, lanes 0..15)
+__device__ __forceinline__ void step_bbm(acc_t& acc, const aop_t& a, const bw_t& b, aop_t& n, bw_t& m, float s0,
+                                         float s1, uint32_t aaddr, uint32_t caddr, const Ctx& c, const Win& w) {
   uint32_t msv;
   uint64_t ex;
-  asm volatile(H3Q_STEP_BB_M_ASM
+  asm volatile(H3Q_STEP_BB_C1M_ASM
                : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [msv] "=&s"(msv), [ex] "=&s"(ex)
                : H3Q_A_IN(a), H3Q_B_IN(b), [s0] "v"(s0), [s1] "v"(s1), [aaddr] "v"(aaddr), [caddr] "v"(caddr),
-                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, 6)
+                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, 9), H3Q_COPY(1, 10)
                : H3Q_STEP_CLOBBERS);
 }
 // base step, next = first K-step of a new base tile (its scale dwords d0/d1 are read here too);
-// copies 0, 1
-__device__ __forceinline__ void step_bbn2(f32x16 (&acc)[4][2], const bf16x8 (&a)[4], const bw_t& b, bf16x8 (&n)[4],
-                                          bw_t& m, uint32_t (&d)[2], uint32_t aaddr, uint32_t caddr, uint32_t saddr,
+// copies 0..2
+__device__ __forceinline__ void step_bbn3(acc_t& acc, const aop_t& a, const bw_t& b, aop_t& n, bw_t& m,
+                                          uint32_t (&d)[2], uint32_t aaddr, uint32_t caddr, uint32_t saddr,
                                           const Ctx& c, const Win& w) {
   uint32_t msv;
-  asm volatile(H3Q_STEP_BBN_C2_ASM
+  asm volatile(H3Q_STEP_BBN_C3_ASM
                : H3Q_ACC(acc), H3Q_A_OUT(n), H3Q_B_OUT(m), [d0] "=&v"(d[0]), [d1] "=&v"(d[1]), [msv] "=&s"(msv)
                : H3Q_A_IN(a), H3Q_B_IN(b), [aaddr] "v"(aaddr), [caddr] "v"(caddr), [saddr] "v"(saddr),
-                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, 0), H3Q_COPY(1, 1)
+                 [sel] "s"(kPermHighHalves), H3Q_COPY(0, 0), H3Q_COPY(1, 1), H3Q_COPY(2, 2)
                : H3Q_STEP_CLOBBERS);
 }
 // base step, next = a LoRA K-step; copies 0..2
-__device__ __forceinline__ void step_bl3(f32x16 (&acc)[4][2], const bf16x8 (&a)[4], const bw_t& b, bf16x8 (&n)[4],
-                                         bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr, const Ctx& c, const Win& w) {
+__device__ __forceinline__ void step_bl3(acc_t& acc, const aop_t& a, const bw_t& b, aop_t& n, bf16x8 (&k)[2],
+                                         uint32_t aaddr, uint32_t baddr, const Ctx& c, const Win& w) {
   uint32_t msv;
   asm volatile(H3Q_STEP_BL_C3_ASM
                : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [msv] "=&s"(msv)
@@ -276,23 +283,33 @@ __device__ __forceinline__ void step_bl3(f32x16 (&acc)[4][2], const bf16x8 (&a)[
                : H3Q_STEP_CLOBBERS);
 }
 // base step, last of the tile loop
-__device__ __forceinline__ void step_bn(f32x16 (&acc)[4][2], const bf16x8 (&a)[4], const bw_t& b) {
+__device__ __forceinline__ void step_bn(acc_t& acc, const aop_t& a, const bw_t& b) {
   asm volatile(H3Q_STEP_BN_ASM : H3Q_ACC(acc) : H3Q_A_IN(a), H3Q_B_IN(b) : H3Q_STEP_CLOBBERS);
 }
-// LoRA step, next = a LoRA K-step; copies I..I+2
-template <int I>
-__device__ __forceinline__ void step_ll3(f32x16 (&acc)[4][2], const bf16x8 (&a)[4], const bf16x8 (&l)[2],
-                                         bf16x8 (&n)[4], bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr, const Ctx& c,
-                                         const Win& w) {
+// LoRA step, next = a LoRA K-step; copies 3..10 (10: lanes 0..15)
+__device__ __forceinline__ void step_ll8(acc_t& acc, const aop_t& a, const bf16x8 (&l)[2], aop_t& n,
+                                         bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr, const Ctx& c, const Win& w) {
+  uint32_t msv;
+  uint64_t ex;
+  asm volatile(H3Q_STEP_LL_C7M_ASM
+               : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [msv] "=&s"(msv), [ex] "=&s"(ex)
+               : H3Q_A_IN(a), [l0] "v"(l[0]), [l1] "v"(l[1]), [aaddr] "v"(aaddr), [baddr] "v"(baddr),
+                 H3Q_COPY(0, 3), H3Q_COPY(1, 4), H3Q_COPY(2, 5), H3Q_COPY(3, 6), H3Q_COPY(4, 7), H3Q_COPY(5, 8),
+                 H3Q_COPY(6, 9), H3Q_COPY(7, 10)
+               : H3Q_STEP_CLOBBERS);
+}
+// LoRA step, next = a LoRA K-step; copies 0..2
+__device__ __forceinline__ void step_ll3(acc_t& acc, const aop_t& a, const bf16x8 (&l)[2], aop_t& n,
+                                         bf16x8 (&k)[2], uint32_t aaddr, uint32_t baddr, const Ctx& c, const Win& w) {
   uint32_t msv;
   asm volatile(H3Q_STEP_LL_C3_ASM
                : H3Q_ACC(acc), H3Q_A_OUT(n), [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [msv] "=&s"(msv)
                : H3Q_A_IN(a), [l0] "v"(l[0]), [l1] "v"(l[1]), [aaddr] "v"(aaddr), [baddr] "v"(baddr),
-                 H3Q_COPY(0, I), H3Q_COPY(1, I + 1), H3Q_COPY(2, I + 2)
+                 H3Q_COPY(0, 0), H3Q_COPY(1, 1), H3Q_COPY(2, 2)
                : H3Q_STEP_CLOBBERS);
 }
 // LoRA step, last of the tile loop
-__device__ __forceinline__ void step_ln(f32x16 (&acc)[4][2], const bf16x8 (&a)[4], const bf16x8 (&l)[2]) {
+__device__ __forceinline__ void step_ln(acc_t& acc, const aop_t& a, const bf16x8 (&l)[2]) {
   asm volatile(H3Q_STEP_LN_ASM : H3Q_ACC(acc) : H3Q_A_IN(a), [l0] "v"(l[0]), [l1] "v"(l[1]) : H3Q_STEP_CLOBBERS);
 }
 
@@ -301,20 +318,19 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-// Plain output through LDS: the tile goes into the freed stages as bf16 [128][264] (8 padding
+// Plain output through LDS: the tile goes into the freed stages as bf16 [256][264] (8 padding
 // columns per row keep the two row groups of one 2-byte store on different banks), then every
-// thread stores 16 chunks of 8 consecutive output columns with 16-byte stores. Needs the output
+// thread stores 32 chunks of 8 consecutive output columns with 16-byte stores. Needs the output
 // rows 16-byte aligned (n_out a multiple of 8, or of 16 for a gate/up weight, and out aligned).
-constexpr int kOutPitch = 264;
 static_assert(BM * kOutPitch * 2 <= kLdsBytes, "output staging must fit the stages");
 
-__device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const f32x16 (&acc)[4][2],
+__device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const acc_t& acc,
                                                       uint8_t* smem, float scale, int64_t m0, int nt, int wave,
                                                       uint32_t lane) {
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -336,7 +352,7 @@ __device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const
   }
 }
 
-// SwiGLU output through LDS: h = bf16(SiLU(gate) * up) as a bf16 [128][136] tile in the freed stages
+// SwiGLU output through LDS: h = bf16(SiLU(gate) * up) as a bf16 [256][136] tile in the freed stages
 // (wave w holds h columns [32w, 32w + 32)), then 16-byte stores of 8 consecutive h columns. With an
 // emit target the same pass also writes the next projection's base operand
 // xs = bf16(f32(h) * pqs_next[n]) from the stored h bits, i.e. exactly what prescaling the stored h
@@ -345,13 +361,13 @@ __device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const
 constexpr int kHPitch = 136;
 static_assert(BM * kHPitch * 2 <= kLdsBytes, "SwiGLU staging must fit the stages");
 
-__device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, const f32x16 (&acc)[4][2],
+__device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, const acc_t& acc,
                                                        uint8_t* smem, float scale, int64_t m0, int nt, int wave,
                                                        uint32_t lane) {
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = i * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
@@ -400,7 +416,7 @@ __device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, cons
 constexpr int kQkPitch = 257;
 static_assert(64 * kQkPitch * 4 <= kLdsBytes, "Q/K staging must fit the stages");
 
-__device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const f32x16 (&acc)[4][2], uint8_t* smem,
+__device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const acc_t& acc, uint8_t* smem,
                                                       float scale, int64_t m0, int nt, int wave, uint32_t lane,
                                                       bool is_q) {
   float* tile = reinterpret_cast<float*>(smem);
@@ -409,7 +425,7 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
                                  : p.qk_gamma_k + static_cast<int64_t>(nt - p.q_tiles) * BN;
   const int half = p.rope_half;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < BM / 64; ++pass) {
     // every wave is past its last LDS read (pass 0: the last stage handover; pass 1: the barrier
     // after the row threads below), so the tile can be overwritten
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -488,7 +504,7 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
 }
 
 template <int EPI, bool LORA>
-__global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -525,13 +541,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
               static_cast<uint32_t>(p.r_tiles) * kLoraTileBytes);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    {  // base tile slot (4w + h)*64 + lane -> row, chunk (see Ctx)
-      const uint32_t row = (wave * 4 + h) * 8 + (lane >> 3);
+    {  // base tile slot (8w + h)*64 + lane -> row, chunk (see Ctx)
+      const uint32_t row = (wave * 8 + h) * 8 + (lane >> 3);
       const uint32_t chunk = (lane & 7) ^ ((row >> 1) & 7);
       c.vact[h] = (static_cast<uint32_t>(m0) + row) * static_cast<uint32_t>(p.act_ld * 2) + chunk * 16;
     }
-    {  // LoRA t' slot (2w + h)*64 + lane -> 128-byte line, then (row, chunk) of the 64-byte rows
-      const uint32_t line = (wave * 2 + h) * 8 + (lane >> 3);
+    {  // LoRA t' slot (4w + h)*64 + lane -> 128-byte line, then (row, chunk) of the 64-byte rows
+      const uint32_t line = (wave * 4 + h) * 8 + (lane >> 3);
       const uint32_t cl = (lane & 7) ^ ((line >> 1) & 7);
       const uint32_t row = line * 2 + (cl >> 2), chunk = cl & 3;
       c.vlt[h] = (static_cast<uint32_t>(m0) + row) * static_cast<uint32_t>(p.lora_t_ld * 2) + chunk * 16;
@@ -548,17 +564,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
 
   // accumulators: zeroed in place in AGPRs (an MFMA of zero operands with C = 0), so that they live
   // in AGPRs from the first to the last K-step
-  f32x16 acc[4][2];
+  acc_t acc;
   {
     const bf16x8 z = {};
-    asm volatile(
-        "v_mfma_f32_32x32x16_bf16 %[c00], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c01], %[z], %[z], 0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %[c10], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c11], %[z], %[z], 0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %[c20], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c21], %[z], %[z], 0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %[c30], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c31], %[z], %[z], 0"
-        : [c00] "=a"(acc[0][0]), [c01] "=a"(acc[0][1]), [c10] "=a"(acc[1][0]), [c11] "=a"(acc[1][1]),
-          [c20] "=a"(acc[2][0]), [c21] "=a"(acc[2][1]), [c30] "=a"(acc[3][0]), [c31] "=a"(acc[3][1])
-        : [z] "v"(z));
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc[i][j]) : "v"(z));
   }
 
   const uint32_t ncol[2] = {static_cast<uint32_t>(wave * 64) + (lane & 31),
@@ -579,20 +591,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
   const uint32_t off_lora_b = kLdsLoraB + wave * 4096;
   const uint32_t smem0 = lds_addr(smem);
 
-  // Prologue: tiles 0 and 1 (7 copies each, tile 1 possibly a LoRA tile or a re-read), then the
-  // first two copies of tile 2's window; wait for tile 0, read and decode its first K-step in C++.
-  copy_slots<0, kCopiesBase>(c, plan<LORA>(c, 0, smem0));
-  copy_slots<0, kCopiesBase>(c, plan<LORA>(c, 1, smem0 + kStage));
+  // Prologue: tiles 0 and 1 (11 copies each, tile 1 possibly a LoRA tile or a re-read), then the
+  // first three copies of tile 2's window; wait for tile 0, read and decode its first K-step in C++.
+  copy_slots<0, kCopies>(c, plan<LORA>(c, 0, smem0));
+  copy_slots<0, kCopies>(c, plan<LORA>(c, 1, smem0 + kStage));
   Win win = plan<LORA>(c, 2, smem0 + 2 * kStage);
-  copy_slots<0, 2>(c, win);
-  stage_barrier<kCopiesBase + 2>();
+  copy_slots<0, 3>(c, win);
+  stage_barrier<kCopies + 3>();
 
-  bf16x8 aX[4], aY[4], lX[2], lY[2];
+  aop_t aX, aY;
+  bf16x8 lX[2], lY[2];
   uint32_t bX[8], bY[8], sdw[2];
   {
     const uint8_t* st = smem;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aX[i] = *reinterpret_cast<const bf16x8*>(st + off_a64[0] + i * 4096);
+    for (int i = 0; i < RT; ++i) aX[i] = *reinterpret_cast<const bf16x8*>(st + off_a64[0] + i * 4096);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       sdw[j] = *reinterpret_cast<const uint32_t*>(st + off_scales + j * 128);
@@ -602,16 +615,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
     }
   }
 
-  // Tile t lives in stage t % 3. A base tile runs K-steps 0..2 (carrying copies 2..6 of the
+  // Tile t lives in stage t % 3. A base tile runs K-steps 0..2 (carrying copies 3..10 of the
   // window of tile t + 2), then the handover waits for tile t + 1 and plans tile t + 3 into the
-  // stage t just left, and K-step 3 runs (copies 0, 1) while it reads tile t + 1's first K-step.
-  // A LoRA tile runs K-step 0 (copies 3..5), the handover, and K-step 1 (copies 0..2). The last base
-  // tile and the last LoRA tile are peeled so that each loop carries one step shape.
+  // stage t just left, and K-step 3 runs (copies 0..2) while it reads tile t + 1's first K-step.
+  // A LoRA tile runs K-step 0 (copies 3..10), the handover, and K-step 1 (copies 0..2). The last
+  // base tile and the last LoRA tile are peeled so that each loop carries one step shape.
   int s_cur = 0;
   auto base_steps_012 = [&](uint32_t st) {
-    step_bb2<2>(acc, aX, bX, aY, bY, e4m3_byte_to_f32<1>(sdw[0]), e4m3_byte_to_f32<1>(sdw[1]), st + off_a64[1],
+    step_bb3<3>(acc, aX, bX, aY, bY, e4m3_byte_to_f32<1>(sdw[0]), e4m3_byte_to_f32<1>(sdw[1]), st + off_a64[1],
                 st + off_codes + 1 * 2 * kCodeRun, c, win);
-    step_bb2<4>(acc, aY, bY, aX, bX, e4m3_byte_to_f32<2>(sdw[0]), e4m3_byte_to_f32<2>(sdw[1]), st + off_a64[2],
+    step_bb3<6>(acc, aY, bY, aX, bX, e4m3_byte_to_f32<2>(sdw[0]), e4m3_byte_to_f32<2>(sdw[1]), st + off_a64[2],
                 st + off_codes + 2 * 2 * kCodeRun, c, win);
     step_bbm(acc, aX, bX, aY, bY, e4m3_byte_to_f32<3>(sdw[0]), e4m3_byte_to_f32<3>(sdw[1]), st + off_a64[3],
              st + off_codes + 3 * 2 * kCodeRun, c, win);
@@ -621,9 +634,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
     const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
     const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
     base_steps_012(st);
-    stage_barrier<kCopiesBase>();  // tile kt+1 has landed; tile kt+2's window may still be in flight
+    stage_barrier<kCopies>();  // tile kt+1 has landed; tile kt+2's window may still be in flight
     win = plan<LORA>(c, kt + 3, st);
-    step_bbn2(acc, aY, bY, aX, bX, sdw, sn + off_a64[0], sn + off_codes, sn + off_scales, c, win);
+    step_bbn3(acc, aY, bY, aX, bX, sdw, sn + off_a64[0], sn + off_codes, sn + off_scales, c, win);
     s_cur = s_nxt;
   }
   {  // last base tile
@@ -631,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
     const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
     base_steps_012(st);
     if (LORA) {
-      stage_barrier<kCopiesBase>();
+      stage_barrier<kCopies>();
       win = plan<LORA>(c, kt + 3, st);
       step_bl3(acc, aY, bY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0], c, win);
     } else {
@@ -645,14 +658,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
     for (; kt + 1 < total; ++kt) {
       const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
       const uint32_t st = smem0 + s_cur * kStage, sn = smem0 + s_nxt * kStage;
-      step_ll3<3>(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1], c, win);
-      stage_barrier<kCopiesLora>();
+      step_ll8(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1], c, win);
+      stage_barrier<kCopies>();
       win = plan<LORA>(c, kt + 3, st);
-      step_ll3<0>(acc, aY, lY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0], c, win);
+      step_ll3(acc, aY, lY, aX, lX, sn + off_a32[0], sn + off_lora_b + off_a32[0], c, win);
       s_cur = s_nxt;
     }
     const uint32_t st = smem0 + s_cur * kStage;  // last LoRA tile
-    step_ll3<3>(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1], c, win);
+    step_ll8(acc, aX, lX, aY, lY, st + off_a32[1], st + off_lora_b + off_a32[1], c, win);
     stage_barrier<0>();
     step_ln(acc, aY, lY);
   }
@@ -685,7 +698,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4_kernel(GemmParams p) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < RT; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t row = m0 + i * 32 + (r >> 2) * 8 + row_lane + (r & 3);

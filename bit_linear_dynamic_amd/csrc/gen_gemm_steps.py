@@ -1,14 +1,13 @@
 """Writes gemm_w4_steps.inc: the instruction sequences of one 16-deep K-step of the main GEMM.
 
-A K-step is 8 v_mfma_f32_32x32x16_bf16 (4 row tiles x 2 column tiles of one wave) with the work for
+A K-step is 16 v_mfma_f32_32x32x16_bf16 (8 row tiles x 2 column tiles of one wave) with the work for
 the next K-step spread between them: LDS reads of the next A operand (and codes / scales), and the
 decode of the next 4-bit B operand (E2M1 codes -> fp32 via v_cvt_scalef32_pk_f32_fp4 with scale 1,
 times the E4M3 block scale, packed to bf16 by v_perm_b32). Written as one asm block per step so the
 compiler cannot gather the decode into a run that leaves the matrix core idle.
 
 Registers v108..v111 and v120..v127 are private to each block (declared clobbered): v120..v127 are
-decode temporaries, v110/v111 the code dwords, v108/v109 the block scales of a new tile. They sit at
-the top of the 128 architectural VGPRs a wave has when two waves share a SIMD. The running step's W4
+decode temporaries, v110/v111 the code dwords, v108/v109 the block scales of a new tile. The running step's W4
 B operand comes in as two 4-register tuples %[bq0], %[bq1] (the previous block's eight decoded
 outputs, which the compiler allocates in place).
 
@@ -16,13 +15,14 @@ A step can also carry global->LDS copies of a later K-tile (buffer_load_dwordx4 
 address), spread between its MFMAs so that the copies of a tile trickle out over the steps between
 two stage handovers instead of leaving every wave at once. Copy j takes operands %[cmj] (M0 value),
 %[cvj] (per-lane offset), %[csj] (uniform offset) and %[crj] (buffer descriptor); a masked copy runs
-on lanes 0..15 only (exec saved in %[ex]). M0 is saved in %[msv] and restored at the end.
+on lanes 0..15 only (exec saved in %[ex]). M0 is saved in %[msv] and restored at the end. The copies
+of a step go after evenly spaced MFMAs.
 
 Run `python gen_gemm_steps.py` after editing; tests/test_abi_cpu.py checks the .inc is current.
 """
 import os
 
-RT = 4          # row tiles (of 32) per wave
+RT = 8          # row tiles (of 32) per wave
 SCL = (108, 109)   # block scales of a new tile (fp32)
 CODE = (110, 111)  # code dwords of the two column tiles
 TMP = 120          # v120..v127: decode temporaries
@@ -51,8 +51,10 @@ def decode_groups(scale_regs):
     return dec
 
 
-# MFMA positions (0..7) after which the copies of a step go, by copy pattern
-COPY_AT = {"": [], "cc": [1, 5], "ccc": [1, 3, 6], "m": [3]}
+def copy_at(n):
+    """MFMA positions (0 .. 2 RT - 1) after which the n copies of a step go: evenly spaced."""
+    nm = 2 * RT
+    return [(q * nm) // n + (nm // n) // 2 for q in range(n)]
 
 
 def copy_lines(j, masked):
@@ -93,7 +95,7 @@ def step(kind, copies=""):
             extras[i].append(f"ds_read_b128 %[n{i}], %[aaddr] offset:{i*2048}")
         extras[RT].append("ds_read_b128 %[k0], %[baddr]")
         extras[RT + 1].append("ds_read_b128 %[k1], %[baddr] offset:2048")
-    for j, (at, kind_c) in enumerate(zip(COPY_AT[copies], copies)):
+    for j, (at, kind_c) in enumerate(zip(copy_at(len(copies)), copies)):
         extras[at] += copy_lines(j, kind_c == 'm')
     L.append("s_nop 1")
     for s in range(n_mfma):
@@ -111,13 +113,18 @@ def render() -> str:
     out = ["// Generated by gen_gemm_steps.py -- do not edit by hand.",
            "// Step variants: source operand (B = W4 decoded, L = LoRA bf16) x next step",
            "// (B: next K-step of the same base tile, BN: first K-step of a new base tile, L: a LoRA",
-           "// K-step, N: none) x copies carried (C2: two, C3: three, M: one on lanes 0..15).",
+           "// K-step, N: none) x copies carried (Cn: n plain copies, M: then one on lanes 0..15).",
            ""]
     names = {'bb': 'BB', 'bB': 'BBN', 'bl': 'BL', 'bn': 'BN', 'll': 'LL', 'ln': 'LN'}
-    cnames = {"": "", "cc": "_C2", "ccc": "_C3", "m": "_M"}
-    for kind, copies in [('bb', 'cc'), ('bb', 'm'), ('bB', 'cc'), ('bl', 'ccc'), ('bn', ''),
-                         ('ll', 'ccc'), ('ln', '')]:
-        out.append(f"#define H3Q_STEP_{names[kind]}{cnames[copies]}_ASM \\")
+
+    def cname(copies):
+        if not copies:
+            return ""
+        plain = copies.count('c')
+        return f"_C{plain}" + ("M" if copies.endswith('m') else "")
+    for kind, copies in [('bb', 'ccc'), ('bb', 'cm'), ('bB', 'ccc'), ('bl', 'ccc'), ('bn', ''),
+                         ('ll', 'cccccccm'), ('ll', 'ccc'), ('ln', '')]:
+        out.append(f"#define H3Q_STEP_{names[kind]}{cname(copies)}_ASM \\")
         body = step(kind, copies)
         for n, l in enumerate(body):
             out.append(f'  "{l}\\n\\t"' + (" \\" if n + 1 < len(body) else ""))

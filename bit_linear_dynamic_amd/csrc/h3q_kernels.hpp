@@ -9,7 +9,7 @@
 namespace h3q {
 
 // Tile geometry of the main GEMM and of the packed weight layout (see gemm_w4.hip).
-constexpr int kGemmBM = 128;   // rows of x per workgroup tile
+constexpr int kGemmBM = 256;   // rows of x per workgroup tile
 constexpr int kGemmBN = 256;   // output columns (packed weight rows) per workgroup tile
 constexpr int kGemmBK = 64;    // K per pipeline stage
 // Packed codes: for column tile nt and K-tile kt, chunk kc (8 consecutive k) of all 256 rows is one

@@ -409,95 +409,132 @@ __device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, cons
 //   u_i = v_i / sqrt(mean_j v_j^2 + eps) * gamma_i            (v = ts * acc, fp32)
 //   out_i = u_i c_i - u_{i+h} s_i,  out_{i+h} = u_{i+h} c_i + u_i s_i   (i < h = rot/2)
 //   out_i = u_i                                               (rot <= i < 128)
-// with c, s the caller's per-row angle table. The fp32 tile goes through the freed LDS stages 64 rows
-// at a time ([64][257] floats: one padding float per row keeps a column read by 64 rows on 64
-// banks); then two threads per (row, head) normalize and rotate in place, and store 16 bytes at a
-// time.
-constexpr int kQkPitch = 257;
-static_assert(64 * kQkPitch * 4 <= kLdsBytes, "Q/K staging must fit the stages");
+// with c, s the caller's per-row angle table. The fp32 tile goes through the freed LDS 128 rows at
+// a time ([128][260] floats: 16-byte aligned rows, and 16-byte reads of 8 consecutive rows fall on
+// distinct banks), with the tile's 256 gamma values beside it; then one thread per (row, head) sums
+// the head's squares with 16-byte reads, and normalizes, rotates and stores 8 pairs at a time
+// straight to the output (16-byte bf16 stores; a scalar path when h is not a multiple of 8). The
+// row's angle table is loaded into registers before the pass's staging, so its latency hides behind
+// the LDS writes and the barrier.
+constexpr int kQkPitch = 260;
+constexpr int kQkRows = 128;
+constexpr uint32_t kQkGamma = kQkRows * kQkPitch * 4;
+static_assert(kQkGamma + BN * 4 <= kLdsBytes, "Q/K staging must fit the LDS");
+static_assert(BN == kThreads, "one gamma value per thread");
+
+__device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8_bf16(uint16_t* dst, const float (&v)[8]) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_hw(v[2 * e]) | (f32_to_bf16_hw(v[2 * e + 1]) << 16);
+  *reinterpret_cast<u32x4*>(dst) = o;
+}
 
 __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const acc_t& acc, uint8_t* smem,
                                                       float scale, int64_t m0, int nt, int wave, uint32_t lane,
                                                       bool is_q) {
   float* tile = reinterpret_cast<float*>(smem);
+  float* gam = reinterpret_cast<float*>(smem + kQkGamma);
   const int tid = threadIdx.x;
   const float* gamma_tile = is_q ? p.qk_gamma_q + static_cast<int64_t>(nt) * BN
                                  : p.qk_gamma_k + static_cast<int64_t>(nt - p.q_tiles) * BN;
   const int half = p.rope_half;
+  const int head = __builtin_amdgcn_readfirstlane(tid >> 7);  // waves 0, 1: head 0; waves 2, 3: head 1
+  const int row_l = tid & (kQkRows - 1);
+  const bool vec = (half & 7) == 0;
+  const bool vec_tab = vec && ((reinterpret_cast<uintptr_t>(p.rope_cos) | reinterpret_cast<uintptr_t>(p.rope_sin)) & 15) == 0;
 #pragma unroll
-  for (int pass = 0; pass < BM / 64; ++pass) {
+  for (int pass = 0; pass < BM / kQkRows; ++pass) {
+    const int64_t row = m0 + pass * kQkRows + row_l;
+    const float* cr = p.rope_cos + row * half;
+    const float* sr = p.rope_sin + row * half;
+    f32x4 cpre[16], spre[16];  // the row's angle table, 4 pairs per entry (h <= 64)
+    if (vec_tab && row < p.S) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (4 * q < half) {
+          cpre[q] = *reinterpret_cast<const f32x4*>(cr + 4 * q);
+          spre[q] = *reinterpret_cast<const f32x4*>(sr + 4 * q);
+        }
+    }
     // every wave is past its last LDS read (pass 0: the last stage handover; pass 1: the barrier
     // after the row threads below), so the tile can be overwritten
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (pass == 0) gam[tid] = gamma_tile[tid];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int ii = 0; ii < kQkRows / 32; ++ii)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row_l = ii * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
+          const int rl = ii * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
           const int col = wave * 64 + j * 32 + static_cast<int>(lane & 31);
-          tile[row_l * kQkPitch + col] = scale * acc[2 * pass + ii][j][r];
+          tile[rl * kQkPitch + col] = scale * acc[pass * (kQkRows / 32) + ii][j][r];
         }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // Two threads per (row, head): part 0 takes the first half of the rotated pairs and of the
-    // pass-through dims, part 1 the second; both compute the head's sum of squares.
-    const int job = tid & 127, part = __builtin_amdgcn_readfirstlane(tid >> 7);
-    const int row_l = job & 63;
-    const int head = __builtin_amdgcn_readfirstlane(job >> 6);
-    const int64_t row = m0 + pass * 64 + row_l;
-    float* t = tile + row_l * kQkPitch + head * 128;
-    float inv = 0.0f;
     if (row < p.S) {
+      const float* t = tile + row_l * kQkPitch + head * 128;
+      const float* g = gam + head * 128;
       float ss = 0.0f;
-#pragma unroll 16
-      for (int i = 0; i < 128; ++i) ss += t[i] * t[i];
-      inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps);
-    }
-    // both parts have read the whole head before either rewrites its half
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (row < p.S) {
-      const float* g = gamma_tile + head * 128;
-      const float* cr = p.rope_cos + row * half;
-      const float* sr = p.rope_sin + row * half;
-      const int split = (half / 2) & ~7;
-      const int pr0 = part == 0 ? 0 : split, pr1 = part == 0 ? split : half;
-      int i = pr0;
-      if ((half & 3) == 0) {  // 8 pairs at a time with 16-byte table loads (rows stay 16-byte aligned)
-        for (; i + 8 <= pr1; i += 8) {
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr + i), c1 = *reinterpret_cast<const f32x4*>(cr + i + 4);
-          const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr + i), s1 = *reinterpret_cast<const f32x4*>(sr + i + 4);
-          const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-          const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(t + 4 * q);
+        ss += v.x * v.x;
+        ss += v.y * v.y;
+        ss += v.z * v.z;
+        ss += v.w * v.w;
+      }
+      const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps);
+      uint16_t* orow = p.out + row * p.out_ld + static_cast<int64_t>(nt) * BN + head * 128;
+      if (vec) {
+#pragma unroll
+        for (int gi = 0; gi < 8; ++gi) {
+          const int i = gi * 8;
+          if (i >= half) break;
+          float tv[8], th[8], gv[8], gh[8], cs[8], sn[8], lo[8], hi[8];
+          load8(t + i, tv);
+          load8(t + i + half, th);
+          load8(g + i, gv);
+          load8(g + i + half, gh);
+          if (vec_tab) {
+            const f32x4 c0 = cpre[2 * gi], c1 = cpre[2 * gi + 1], s0 = spre[2 * gi], s1 = spre[2 * gi + 1];
+            cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w; cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
+            sn[0] = s0.x; sn[1] = s0.y; sn[2] = s0.z; sn[3] = s0.w; sn[4] = s1.x; sn[5] = s1.y; sn[6] = s1.z; sn[7] = s1.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              cs[e] = cr[i + e];
+              sn[e] = sr[i + e];
+            }
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float a = t[i + e] * inv * g[i + e], b = t[i + e + half] * inv * g[i + e + half];
-            t[i + e] = a * cs[e] - b * sn[e];
-            t[i + e + half] = b * cs[e] + a * sn[e];
+            const float a = tv[e] * inv * gv[e], b = th[e] * inv * gh[e];
+            lo[e] = a * cs[e] - b * sn[e];
+            hi[e] = b * cs[e] + a * sn[e];
           }
+          store8_bf16(orow + i, lo);
+          store8_bf16(orow + i + half, hi);
         }
-      }
-      for (; i < pr1; ++i) {
-        const float a = t[i] * inv * g[i], b = t[i + half] * inv * g[i + half];
-        const float c = cr[i], s = sr[i];
-        t[i] = a * c - b * s;
-        t[i + half] = b * c + a * s;
-      }
-      const int rest = 128 - 2 * half;
-      const int q0 = 2 * half + (part == 0 ? 0 : rest / 2), q1 = part == 0 ? 2 * half + rest / 2 : 128;
-      for (int k = q0; k < q1; ++k) t[k] = t[k] * inv * g[k];
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (row < p.S) {  // the head's 16 chunks of 8: part 0 stores the first 8, part 1 the rest
-      uint16_t* orow = p.out + row * p.out_ld + static_cast<int64_t>(nt) * BN + head * 128;
+        for (int k = 2 * half; k < 128; k += 8) {
+          float tv[8], gv[8], u[8];
+          load8(t + k, tv);
+          load8(g + k, gv);
 #pragma unroll
-      for (int qq = 0; qq < 8; ++qq) {
-        const int q = part * 8 + qq;
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = f32_to_bf16_hw(t[q * 8 + 2 * e]) | (f32_to_bf16_hw(t[q * 8 + 2 * e + 1]) << 16);
-        *reinterpret_cast<u32x4*>(orow + q * 8) = o;
+          for (int e = 0; e < 8; ++e) u[e] = tv[e] * inv * gv[e];
+          store8_bf16(orow + k, u);
+        }
+      } else {  // h not a multiple of 8: one pair at a time, 2-byte stores
+        for (int i = 0; i < half; ++i) {
+          const float a = t[i] * inv * g[i], b = t[i + half] * inv * g[i + half];
+          const float c = cr[i], sv = sr[i];
+          orow[i] = static_cast<uint16_t>(f32_to_bf16_hw(a * c - b * sv));
+          orow[i + half] = static_cast<uint16_t>(f32_to_bf16_hw(b * c + a * sv));
+        }
+        for (int k = 2 * half; k < 128; ++k) orow[k] = static_cast<uint16_t>(f32_to_bf16_hw(t[k] * inv * g[k]));
       }
     }
   }

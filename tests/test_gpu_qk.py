@@ -32,14 +32,25 @@ def gammas(q_width, seed):
     return g[0].contiguous(), g[1].contiguous()
 
 
-def run_case(p: Proj, x, pqs, q_width, rot, adapter_id, strength, flags=0, rows=None):
+def off_by_one_float(t):
+    """A device copy of t whose data starts 4 bytes past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+    v = buf[1:].view(t.shape)
+    v.copy_(t.to("cuda"))
+    assert v.data_ptr() % 16 == 4
+    return v
+
+
+def run_case(p: Proj, x, pqs, q_width, rot, adapter_id, strength, flags=0, rows=None, misaligned_tables=False):
     S = x.shape[0]
     gq, gk = gammas(q_width, 900 + q_width + rot)
     cos, sin = synth.rope_table(S, rot)
     dev = "cuda"
+    cos_d, sin_d = (cos.to(dev), sin.to(dev)) if rot else (None, None)
+    if rot and misaligned_tables:
+        cos_d, sin_d = off_by_one_float(cos), off_by_one_float(sin)
     y = h3q.h3q_linear_qk_norm_rope(x.to(dev), pqs.to(dev) if pqs is not None else None, p.handle, adapter_id,
-                                    strength, q_width, rot, EPS, gq.to(dev), gk.to(dev),
-                                    cos.to(dev) if rot else None, sin.to(dev) if rot else None, flags=flags)
+                                    strength, q_width, rot, EPS, gq.to(dev), gk.to(dev), cos_d, sin_d, flags=flags)
     plain = h3q.h3q_linear_ex(x.to(dev), pqs.to(dev) if pqs is not None else None, p.handle, adapter_id, strength,
                               flags)
     torch.cuda.synchronize()
@@ -67,6 +78,8 @@ CASES = [
     (129, 256, 512, 0, 128, 64),
     (64, 320, 256, 0, 0, 64),
     (513, 1024, 768, 0, 96, 384),
+    (200, 256, 256, 0, 100, 64),   # rot/2 = 50, not a multiple of 8: the one-pair-at-a-time path
+    (90, 256, 256, 0, 16, 64),     # rot/2 = 8: one group of 8 pairs, 112 pass-through dims
 ]
 
 
@@ -81,6 +94,19 @@ def test_qk_norm_rope_parity(S, K, q_width, extra, rot, rank):
         pqs = synth.pre_quant_scale(K, 1104)
         for aid, st in ((NONE, 0.0), (1, 1.0)):
             run_case(p, x, pqs, q_width, rot, aid, st)
+    finally:
+        p.free()
+
+
+def test_qk_norm_rope_misaligned_tables():
+    """Angle tables that start 4 bytes past a 16-byte boundary take scalar table loads."""
+    S, K, q_width = 150, 256, 256
+    say("qk misaligned angle tables")
+    p = Proj(3 * q_width, K, 1300)
+    try:
+        p.add_adapter(1, 64, 64.0, 1301, 1302)
+        run_case(p, synth.activation(S, K, 1303), synth.pre_quant_scale(K, 1304), q_width, 96, 1, 1.0,
+                 misaligned_tables=True)
     finally:
         p.free()
 

@@ -601,13 +601,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
 
   // accumulators: zeroed in place in AGPRs (an MFMA of zero operands with C = 0), so that they live
   // in AGPRs from the first to the last K-step
+  // One asm block: the compiler writes z just before it and does not see the MFMAs inside, so the
+  // block itself waits out the VALU-write -> MFMA-read hazard (s_nop 4) before the first MFMA (without
+  // it, a schedule that put the write of z right before the block left acc[0][0] holding garbage).
   acc_t acc;
   {
     const bf16x8 z = {};
-#pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc[i][j]) : "v"(z));
+    asm volatile(
+        "s_nop 4\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c00], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c01], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c10], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c11], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c20], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c21], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c30], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c31], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c40], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c41], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c50], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c51], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c60], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c61], %[z], %[z], 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c70], %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %[c71], %[z], %[z], 0"
+        : [c00] "=a"(acc[0][0]), [c01] "=a"(acc[0][1]), [c10] "=a"(acc[1][0]), [c11] "=a"(acc[1][1]),
+          [c20] "=a"(acc[2][0]), [c21] "=a"(acc[2][1]), [c30] "=a"(acc[3][0]), [c31] "=a"(acc[3][1]),
+          [c40] "=a"(acc[4][0]), [c41] "=a"(acc[4][1]), [c50] "=a"(acc[5][0]), [c51] "=a"(acc[5][1]),
+          [c60] "=a"(acc[6][0]), [c61] "=a"(acc[6][1]), [c70] "=a"(acc[7][0]), [c71] "=a"(acc[7][1])
+        : [z] "v"(z));
   }
 
   const uint32_t ncol[2] = {static_cast<uint32_t>(wave * 64) + (lane & 31),

@@ -30,9 +30,9 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per GEMM launch of this workload from rocprofv3 FETCH_SIZE (x 2.00) and WRITE_SIZE (x 1.00)
 # counter runs, mean over the four projections (profiles/gemm_w4_block_S37726.md), valid only for the
 # GEMM sources they were taken with (SHA-256 prefix of the files below, in this order).
-GEMM_TRAFFIC_BYTES = 9.024e9
+GEMM_TRAFFIC_BYTES = 9.026e9
 GEMM_TRAFFIC_SOURCES = ("gemm_w4.hip", "gemm_w4_steps.inc", "h3q_device.hpp", "h3q_kernels.hpp")
-GEMM_TRAFFIC_SHA = "435e944e31942d4e"
+GEMM_TRAFFIC_SHA = "be0a84328521c700"
 
 
 def gemm_traffic():

@@ -53,9 +53,10 @@ constexpr uint32_t kLdsLoraB = BM * kLoraBK * 2;         // LoRA tile: B after t
 constexpr uint32_t kStage = kLdsScales + kScaleTileBytes; // 43008
 constexpr int kStages = 3;
 constexpr int kGroupM = 2;  // row tiles per group in the work order
-// The plain output staging (bf16 [256][264], below) is larger than the three stages.
-constexpr int kOutPitch = 264;
-constexpr uint32_t kLdsBytes = kStages * kStage > BM * kOutPitch * 2 ? kStages * kStage : BM * kOutPitch * 2;
+// The plain output staging (128 row pairs x 264 dwords, below) is larger than the three stages.
+constexpr int kPairPitch = 264;
+constexpr uint32_t kOutStaging = BM / 2 * kPairPitch * 4;
+constexpr uint32_t kLdsBytes = kStages * kStage > kOutStaging ? kStages * kStage : kOutStaging;
 static_assert(kLdsLoraB + kLoraTileBytes <= kLdsCodes, "LoRA tile must leave the code and scale areas free");
 static_assert(kLdsBytes <= 160 * 1024, "the workgroup must fit a CU's LDS");
 // DMA instructions per wave per copy window (every window issues the same number, so that a wave can
@@ -318,88 +319,120 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-// Plain output through LDS: the tile goes into the freed stages as bf16 [256][264] (8 padding
-// columns per row keep the two row groups of one 2-byte store on different banks), then every
-// thread stores 32 chunks of 8 consecutive output columns with 16-byte stores. Needs the output
-// rows 16-byte aligned (n_out a multiple of 8, or of 16 for a gate/up weight, and out aligned).
-static_assert(BM * kOutPitch * 2 <= kLdsBytes, "output staging must fit the stages");
+// Two fp32 values as a bf16 pair (low half: lo), one hardware conversion (round to nearest even).
+__device__ __forceinline__ uint32_t bf16x2_hw(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Plain output through LDS: the tile goes into the freed stages as row pairs -- dword [q][c] holds
+// column c of rows 2q (low half) and 2q + 1 (high half), 264 dwords per pair (8 of padding) -- so
+// that each lane writes its accumulator registers r, r + 1 (two consecutive rows of one column) with
+// one conversion and one 4-byte write. Then every thread reads 8 dwords of a row pair (two 16-byte
+// reads), splits them into the two rows' chunks of 8 consecutive columns (v_perm_b32) and stores both
+// with 16-byte stores. Needs the output rows 16-byte aligned (n_out a multiple of 8, or of 16 for a
+// gate/up weight, and out aligned).
+static_assert(kOutStaging <= kLdsBytes, "output staging must fit the LDS");
+constexpr uint32_t kPermLowHalves = 0x05040100u;   // v_perm_b32: low 16 bits of each source
 
 __device__ __forceinline__ void plain_epilogue_staged(const GemmParams& p, const acc_t& acc,
                                                       uint8_t* smem, float scale, int64_t m0, int nt, int wave,
                                                       uint32_t lane) {
-  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  uint32_t* tile = reinterpret_cast<uint32_t*>(smem);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
+      for (int r = 0; r < 16; r += 2) {
+        const int row = i * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);  // even
         const int col = wave * 64 + j * 32 + static_cast<int>(lane & 31);
-        tile[row * kOutPitch + col] = static_cast<uint16_t>(f32_to_bf16_hw(scale * acc[i][j][r]));
+        tile[(row >> 1) * kPairPitch + col] = bf16x2_hw(scale * acc[i][j][r], scale * acc[i][j][r + 1]);
       }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int q = 0; q < BM * BN / 8 / kThreads; ++q) {
+  for (int q = 0; q < BM * BN / 16 / kThreads; ++q) {
     const int c = static_cast<int>(threadIdx.x) + kThreads * q;
-    const int row = c >> 5, c8 = (c & 31) * 8;
-    const int64_t grow = m0 + row;
+    const int rp = c >> 5, c8 = (c & 31) * 8;
+    const u32x4 d0 = *reinterpret_cast<const u32x4*>(tile + rp * kPairPitch + c8);
+    const u32x4 d1 = *reinterpret_cast<const u32x4*>(tile + rp * kPairPitch + c8 + 4);
+    const u32x4 even = {__builtin_amdgcn_perm(d0.y, d0.x, kPermLowHalves), __builtin_amdgcn_perm(d0.w, d0.z, kPermLowHalves),
+                        __builtin_amdgcn_perm(d1.y, d1.x, kPermLowHalves), __builtin_amdgcn_perm(d1.w, d1.z, kPermLowHalves)};
+    const u32x4 odd = {__builtin_amdgcn_perm(d0.y, d0.x, kPermHighHalves), __builtin_amdgcn_perm(d0.w, d0.z, kPermHighHalves),
+                       __builtin_amdgcn_perm(d1.y, d1.x, kPermHighHalves), __builtin_amdgcn_perm(d1.w, d1.z, kPermHighHalves)};
+    const int64_t grow = m0 + 2 * rp;
     const int64_t n = packed_row_source(nt, c8, p.gate_up != 0, p.n_out);
-    if (grow < p.S && n >= 0)
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile + row * kOutPitch + c8),
-                                  reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n));
+    if (n >= 0) {
+      if (grow < p.S) __builtin_nontemporal_store(even, reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n));
+      if (grow + 1 < p.S) __builtin_nontemporal_store(odd, reinterpret_cast<u32x4*>(p.out + (grow + 1) * p.out_ld + n));
+    }
   }
 }
 
-// SwiGLU output through LDS: h = bf16(SiLU(gate) * up) as a bf16 [256][136] tile in the freed stages
-// (wave w holds h columns [32w, 32w + 32)), then 16-byte stores of 8 consecutive h columns. With an
+// SwiGLU output through LDS: h = bf16(SiLU(gate) * up) staged as row pairs like the plain output
+// (dword [q][c] = h column c of rows 2q and 2q + 1; 128 h columns + 8 of padding per pair; wave w holds
+// h columns [32w, 32w + 32)), then 16-byte stores of 8 consecutive h columns of both rows. With an
 // emit target the same pass also writes the next projection's base operand
 // xs = bf16(f32(h) * pqs_next[n]) from the stored h bits, i.e. exactly what prescaling the stored h
 // would give (FL2VA Turbo, "Implementation": the producer emitting the base input beside the exact bf16
 // LoRA input). Needs n_out % 8 == 0 and 16-byte aligned rows.
-constexpr int kHPitch = 136;
-static_assert(BM * kHPitch * 2 <= kLdsBytes, "SwiGLU staging must fit the stages");
+constexpr int kHPairPitch = 136;
+static_assert(BM / 2 * kHPairPitch * 4 <= kLdsBytes, "SwiGLU staging must fit the stages");
+
+// One 16-byte chunk of h (8 columns from n) of output row grow, and its emitted prescaled copy.
+__device__ __forceinline__ void swiglu_store_chunk(const GemmParams& p, const u32x4& hv, int64_t grow, int64_t n) {
+  __builtin_nontemporal_store(hv, reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n));
+  if (p.emit_out) {
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(p.emit_pqs + n);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(p.emit_pqs + n + 4);
+    const float pq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+    uint32_t xw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      xw[e] = f32_to_bf16_hw(bf16_bits_to_f32(hw[e] & 0xffffu) * pq[2 * e]) |
+              (f32_to_bf16_hw(bf16_bits_to_f32(hw[e] >> 16) * pq[2 * e + 1]) << 16);
+    __builtin_nontemporal_store(u32x4{xw[0], xw[1], xw[2], xw[3]},
+                                reinterpret_cast<u32x4*>(p.emit_out + grow * p.emit_ld + n));
+  }
+}
 
 __device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, const acc_t& acc,
                                                        uint8_t* smem, float scale, int64_t m0, int nt, int wave,
                                                        uint32_t lane) {
-  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  uint32_t* tile = reinterpret_cast<uint32_t*>(smem);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = i * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);
+    for (int r = 0; r < 16; r += 2) {
+      const int row = i * 32 + (r >> 2) * 8 + static_cast<int>(lane >> 5) * 4 + (r & 3);  // even
       const int col = wave * 32 + static_cast<int>(lane & 31);
-      const float g = scale * acc[i][0][r];
-      const float u = scale * acc[i][1][r];
-      tile[row * kHPitch + col] = static_cast<uint16_t>(f32_to_bf16_hw(silu(g) * u));
-      if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // 4 values at a time: accumulators stay in AGPRs
+      const float g0 = scale * acc[i][0][r], u0 = scale * acc[i][1][r];
+      const float g1 = scale * acc[i][0][r + 1], u1 = scale * acc[i][1][r + 1];
+      tile[(row >> 1) * kHPairPitch + col] = bf16x2_hw(silu(g0) * u0, silu(g1) * u1);
+      if ((r & 3) == 2) __builtin_amdgcn_sched_barrier(0);  // 4 values at a time: accumulators stay in AGPRs
     }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int q = 0; q < BM * (BN / 2) / 8 / kThreads; ++q) {
+  for (int q = 0; q < BM * (BN / 2) / 16 / kThreads; ++q) {
     const int c = static_cast<int>(threadIdx.x) + kThreads * q;
-    const int row = c >> 4, c8 = (c & 15) * 8;
-    const int64_t grow = m0 + row;
+    const int rp = c >> 4, c8 = (c & 15) * 8;
     const int64_t n = static_cast<int64_t>(nt) * (BN / 2) + c8;
-    if (grow >= p.S || n >= p.n_out) continue;
-    const u32x4 hv = *reinterpret_cast<const u32x4*>(tile + row * kHPitch + c8);
-    __builtin_nontemporal_store(hv, reinterpret_cast<u32x4*>(p.out + grow * p.out_ld + n));
-    if (p.emit_out) {
-      const f32x4 q0 = *reinterpret_cast<const f32x4*>(p.emit_pqs + n);
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(p.emit_pqs + n + 4);
-      const float pq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-      uint32_t xw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        xw[e] = f32_to_bf16_hw(bf16_bits_to_f32(hw[e] & 0xffffu) * pq[2 * e]) |
-                (f32_to_bf16_hw(bf16_bits_to_f32(hw[e] >> 16) * pq[2 * e + 1]) << 16);
-      __builtin_nontemporal_store(u32x4{xw[0], xw[1], xw[2], xw[3]},
-                                  reinterpret_cast<u32x4*>(p.emit_out + grow * p.emit_ld + n));
-    }
+    if (n >= p.n_out) continue;
+    const u32x4 d0 = *reinterpret_cast<const u32x4*>(tile + rp * kHPairPitch + c8);
+    const u32x4 d1 = *reinterpret_cast<const u32x4*>(tile + rp * kHPairPitch + c8 + 4);
+    const int64_t grow = m0 + 2 * rp;
+    if (grow < p.S)
+      swiglu_store_chunk(p, u32x4{__builtin_amdgcn_perm(d0.y, d0.x, kPermLowHalves), __builtin_amdgcn_perm(d0.w, d0.z, kPermLowHalves),
+                                  __builtin_amdgcn_perm(d1.y, d1.x, kPermLowHalves), __builtin_amdgcn_perm(d1.w, d1.z, kPermLowHalves)},
+                         grow, n);
+    if (grow + 1 < p.S)
+      swiglu_store_chunk(p, u32x4{__builtin_amdgcn_perm(d0.y, d0.x, kPermHighHalves), __builtin_amdgcn_perm(d0.w, d0.z, kPermHighHalves),
+                                  __builtin_amdgcn_perm(d1.y, d1.x, kPermHighHalves), __builtin_amdgcn_perm(d1.w, d1.z, kPermHighHalves)},
+                         grow + 1, n);
   }
 }
 
@@ -720,8 +753,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
     stage_barrier<0>();
     step_ln(acc, aY, lY);
   }
-  // the last MFMAs must retire before their accumulators are read by ordinary instructions
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // the last MFMAs must retire before their accumulators are read by ordinary instructions (the
+  // accumulators are operands, so no read of them can be scheduled above the wait)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : H3Q_ACC(acc)::"memory");
 
   // Epilogue. Accumulator register r of lane l in a 32x32 tile holds
   // row (r/4)*8 + (l/32)*4 + r%4, column l%32.

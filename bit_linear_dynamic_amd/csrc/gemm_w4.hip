@@ -445,10 +445,10 @@ __device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, cons
 // with c, s the caller's per-row angle table. The fp32 tile goes through the freed LDS 128 rows at
 // a time ([128][260] floats: 16-byte aligned rows, and 16-byte reads of 8 consecutive rows fall on
 // distinct banks), with the tile's 256 gamma values beside it; then one thread per (row, head) sums
-// the head's squares with 16-byte reads, and normalizes, rotates and stores 8 pairs at a time
-// straight to the output (16-byte bf16 stores; a scalar path when h is not a multiple of 8). The
-// row's angle table is loaded into registers before the pass's staging, so its latency hides behind
-// the LDS writes and the barrier.
+// the head's squares with 16-byte reads, and normalizes and rotates 8 pairs at a time in place (one
+// pair at a time when h is not a multiple of 8); then the tile is stored as bf16 by 32 threads per
+// row, whole row segments per store instruction. The row's angle table is loaded into registers
+// before the pass's staging, so its latency hides behind the LDS writes and the barrier.
 constexpr int kQkPitch = 260;
 constexpr int kQkRows = 128;
 constexpr uint32_t kQkGamma = kQkRows * kQkPitch * 4;
@@ -458,6 +458,10 @@ static_assert(BN == kThreads, "one gamma value per thread");
 __device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 __device__ __forceinline__ void store8_bf16(uint16_t* dst, const float (&v)[8]) {
   u32x4 o;
@@ -509,7 +513,7 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
         }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (row < p.S) {
-      const float* t = tile + row_l * kQkPitch + head * 128;
+      float* t = tile + row_l * kQkPitch + head * 128;
       const float* g = gam + head * 128;
       float ss = 0.0f;
 #pragma unroll
@@ -521,7 +525,6 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
         ss += v.w * v.w;
       }
       const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps);
-      uint16_t* orow = p.out + row * p.out_ld + static_cast<int64_t>(nt) * BN + head * 128;
       if (vec) {
 #pragma unroll
         for (int gi = 0; gi < 8; ++gi) {
@@ -549,8 +552,8 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
             lo[e] = a * cs[e] - b * sn[e];
             hi[e] = b * cs[e] + a * sn[e];
           }
-          store8_bf16(orow + i, lo);
-          store8_bf16(orow + i + half, hi);
+          store8(t + i, lo);
+          store8(t + i + half, hi);
         }
         for (int k = 2 * half; k < 128; k += 8) {
           float tv[8], gv[8], u[8];
@@ -558,16 +561,30 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
           load8(g + k, gv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) u[e] = tv[e] * inv * gv[e];
-          store8_bf16(orow + k, u);
+          store8(t + k, u);
         }
-      } else {  // h not a multiple of 8: one pair at a time, 2-byte stores
+      } else {  // h not a multiple of 8: one pair at a time
         for (int i = 0; i < half; ++i) {
           const float a = t[i] * inv * g[i], b = t[i + half] * inv * g[i + half];
           const float c = cr[i], sv = sr[i];
-          orow[i] = static_cast<uint16_t>(f32_to_bf16_hw(a * c - b * sv));
-          orow[i + half] = static_cast<uint16_t>(f32_to_bf16_hw(b * c + a * sv));
+          t[i] = a * c - b * sv;
+          t[i + half] = b * c + a * sv;
         }
-        for (int k = 2 * half; k < 128; ++k) orow[k] = static_cast<uint16_t>(f32_to_bf16_hw(t[k] * inv * g[k]));
+        for (int k = 2 * half; k < 128; ++k) t[k] = t[k] * inv * g[k];
+      }
+    }
+    // The results overwrote their own inputs in the tile; now 32 threads per row store 8 consecutive
+    // columns each, so every store instruction covers whole 512-byte row segments.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < kQkRows * BN / 8 / kThreads; ++k) {
+      const int cidx = tid + kThreads * k;
+      const int rl = cidx >> 5, c8 = (cidx & 31) * 8;
+      const int64_t grow = m0 + pass * kQkRows + rl;
+      if (grow < p.S) {
+        float v[8];
+        load8(tile + rl * kQkPitch + c8, v);
+        store8_bf16(p.out + grow * p.out_ld + static_cast<int64_t>(nt) * BN + c8, v);
       }
     }
   }

@@ -176,14 +176,17 @@ template <int I> __device__ __forceinline__ u32x4 slot_rsrc(const Ctx& c, const 
   [cm##j] "s"(slot_m0<I>(w)), [cv##j] "v"(slot_voff<I>(c, w)), [cs##j] "s"(slot_soff<I>(w)),      \
       [cr##j] "s"(slot_rsrc<I>(c, w))
 
-// One copy on its own (prologue). M0 is saved and restored around it.
+// One copy on its own (prologue). M0 is saved and restored around it. The leading wait covers an SGPR
+// operand that the compiler may have just written with a VALU instruction (v_readlane after a spill,
+// v_readfirstlane), which a vector-memory instruction must not read for 5 wait states; the compiler
+// does not look inside the block to insert them.
 template <int I>
 __device__ __forceinline__ void copy_slot(const Ctx& c, const Win& w) {
   uint32_t msv;
   if constexpr (I == 10) {
     uint64_t ex;
     asm volatile(
-        "s_mov_b32 %[msv], m0\n\ts_mov_b64 %[ex], exec\n\ts_mov_b32 exec_lo, 0xffff\n\ts_mov_b32 exec_hi, 0\n\t"
+        "s_nop 4\n\ts_mov_b32 %[msv], m0\n\ts_mov_b64 %[ex], exec\n\ts_mov_b32 exec_lo, 0xffff\n\ts_mov_b32 exec_hi, 0\n\t"
         "s_mov_b32 m0, %[cm0]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[cv0], %[cr0], %[cs0] offen lds\n\t"
         "s_mov_b64 exec, %[ex]\n\ts_mov_b32 m0, %[msv]"
         : [msv] "=&s"(msv), [ex] "=&s"(ex)
@@ -191,7 +194,7 @@ __device__ __forceinline__ void copy_slot(const Ctx& c, const Win& w) {
         : "memory");
   } else {
     asm volatile(
-        "s_mov_b32 %[msv], m0\n\ts_mov_b32 m0, %[cm0]\n\ts_nop 0\n\t"
+        "s_nop 4\n\ts_mov_b32 %[msv], m0\n\ts_mov_b32 m0, %[cm0]\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %[cv0], %[cr0], %[cs0] offen lds\n\ts_mov_b32 m0, %[msv]"
         : [msv] "=&s"(msv)
         : H3Q_COPY(0, I)

@@ -84,7 +84,9 @@ __device__ __forceinline__ uint32_t lds_chunk_offset32(uint32_t row, uint32_t ch
 // operations themselves (the compiler neither sees nor waits on them): global->LDS copies
 // (buffer_load_dwordx4 ... lds, 16 bytes per lane to LDS address M0 + 16 * lane) and 16-byte
 // buffer stores. M0 is saved and restored around each copy. A raw buffer descriptor returns zero
-// for reads past its size and drops writes past it.
+// for reads past its size and drops writes past it. Each block opens with s_nop 4: a vector-memory
+// instruction must not read an SGPR for 5 wait states after a VALU instruction wrote it (v_readlane
+// after a spill, v_readfirstlane), and the compiler does not look inside the block to insert them.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 buf_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -95,7 +97,7 @@ __device__ __forceinline__ u32x4 buf_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
   uint32_t msv;
   asm volatile(
-      "s_mov_b32 %[msv], m0\n\ts_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
+      "s_nop 4\n\ts_mov_b32 %[msv], m0\n\ts_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
       "buffer_load_dwordx4 %[v], %[r], %[s] offen lds\n\ts_mov_b32 m0, %[msv]"
       : [msv] "=&s"(msv)
       : [m] "s"(lds), [v] "v"(voff), [r] "s"(r), [s] "s"(soff)
@@ -109,7 +111,7 @@ __device__ __forceinline__ void dma16_lanes(u32x4 r, uint32_t lds, uint32_t voff
   uint32_t msv;
   uint64_t ex;
   asm volatile(
-      "s_mov_b32 %[msv], m0\n\ts_mov_b64 %[ex], exec\n\ts_mov_b32 exec_lo, %[lm]\n\ts_mov_b32 exec_hi, 0\n\t"
+      "s_nop 4\n\ts_mov_b32 %[msv], m0\n\ts_mov_b64 %[ex], exec\n\ts_mov_b32 exec_lo, %[lm]\n\ts_mov_b32 exec_hi, 0\n\t"
       "s_mov_b32 m0, %[m]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v], %[r], %[s] offen lds\n\t"
       "s_mov_b64 exec, %[ex]\n\ts_mov_b32 m0, %[msv]"
       : [msv] "=&s"(msv), [ex] "=&s"(ex)
@@ -120,7 +122,7 @@ __device__ __forceinline__ void dma16_lanes(u32x4 r, uint32_t lds, uint32_t voff
 
 // Store 16 bytes per lane at buffer offset voff + soff.
 __device__ __forceinline__ void buf_store16(u32x4 data, u32x4 r, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_store_dwordx4 %[d], %[v], %[r], %[s] offen"
+  asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %[d], %[v], %[r], %[s] offen"
                :
                : [d] "v"(data), [v] "v"(voff), [r] "s"(r), [s] "s"(soff)
                : "memory");

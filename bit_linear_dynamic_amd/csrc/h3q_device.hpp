@@ -87,6 +87,8 @@ __device__ __forceinline__ uint32_t lds_chunk_offset32(uint32_t row, uint32_t ch
 // for reads past its size and drops writes past it. Each block opens with s_nop 4: a vector-memory
 // instruction must not read an SGPR for 5 wait states after a VALU instruction wrote it (v_readlane
 // after a spill, v_readfirstlane), and the compiler does not look inside the block to insert them.
+// A store closes with s_nop 1: a store of more than 64 bits reads its data VGPRs after issue, and
+// they may not be overwritten by a VALU instruction for one wait state.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 buf_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -122,7 +124,7 @@ __device__ __forceinline__ void dma16_lanes(u32x4 r, uint32_t lds, uint32_t voff
 
 // Store 16 bytes per lane at buffer offset voff + soff.
 __device__ __forceinline__ void buf_store16(u32x4 data, u32x4 r, uint32_t voff, uint32_t soff) {
-  asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %[d], %[v], %[r], %[s] offen"
+  asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %[d], %[v], %[r], %[s] offen\n\ts_nop 1"
                :
                : [d] "v"(data), [v] "v"(voff), [r] "s"(r), [s] "s"(soff)
                : "memory");

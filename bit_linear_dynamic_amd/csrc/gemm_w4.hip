@@ -322,12 +322,6 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-// Two fp32 values as a bf16 pair (low half: lo), one hardware conversion (round to nearest even).
-__device__ __forceinline__ uint32_t bf16x2_hw(float lo, float hi) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
 
 // Plain output through LDS: the tile goes into the freed stages as row pairs -- dword [q][c] holds
 // column c of rows 2q (low half) and 2q + 1 (high half), 264 dwords per pair (8 of padding) -- so
@@ -395,8 +389,7 @@ __device__ __forceinline__ void swiglu_store_chunk(const GemmParams& p, const u3
     uint32_t xw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      xw[e] = f32_to_bf16_hw(bf16_bits_to_f32(hw[e] & 0xffffu) * pq[2 * e]) |
-              (f32_to_bf16_hw(bf16_bits_to_f32(hw[e] >> 16) * pq[2 * e + 1]) << 16);
+      xw[e] = bf16x2_hw(bf16_bits_to_f32(hw[e] & 0xffffu) * pq[2 * e], __uint_as_float(hw[e] & 0xffff0000u) * pq[2 * e + 1]);
     __builtin_nontemporal_store(u32x4{xw[0], xw[1], xw[2], xw[3]},
                                 reinterpret_cast<u32x4*>(p.emit_out + grow * p.emit_ld + n));
   }
@@ -469,7 +462,7 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
 __device__ __forceinline__ void store8_bf16(uint16_t* dst, const float (&v)[8]) {
   u32x4 o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_hw(v[2 * e]) | (f32_to_bf16_hw(v[2 * e + 1]) << 16);
+  for (int e = 0; e < 4; ++e) o[e] = bf16x2_hw(v[2 * e], v[2 * e + 1]);
   *reinterpret_cast<u32x4*>(dst) = o;
 }
 

@@ -21,19 +21,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Scalar conversions
 // ---------------------------------------------------------------------------------------------
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // fp32 -> bf16 bits by the hardware conversion (v_cvt_pk_bf16_f32: round to nearest even).
 __device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two fp32 values as a bf16 pair (low half: lo), one hardware conversion (round to nearest even).
+__device__ __forceinline__ uint32_t bf16x2_hw(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // E4M3 ("FN": bias 7, no inf, NaN = 0x7F) scale in byte SEL of w -> fp32. gfx950's

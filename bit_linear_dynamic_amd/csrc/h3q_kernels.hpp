@@ -70,8 +70,8 @@ struct LoraDownParams {
   const float* f_div_dev;
   uint16_t* t_out;          // bf16 [S][r_pad]
   uint16_t* xs_out;         // bf16 [S][K_pad] = x * pqs, or null
+  int64_t bm;               // rows per workgroup (set by launch_lora_down)
 };
-constexpr int kLoraBM = 128;
 hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream);
 
 struct PrescaleParams {

@@ -7,9 +7,10 @@
 // The same pass writes the base path's operand xs = bf16(x * pqs) (same section: pre_quant_scale
 // applies to the base path only), since it is already reading every element of x.
 //
-// Geometry: one workgroup of 4 wave64s per CU and RTM row tiles of 32 per workgroup, RTM chosen
-// from S so that the row tiles spread over the CUs in one round. Every wave computes all RTM row
-// tiles for its columns: the r_pad/32 column tiles of 32 go to the waves round-robin, at most NC per
+// Geometry: one workgroup of 4 wave64s per CU, bm = ceil(S / CUs) rows per workgroup (at least 32,
+// at most what the accumulators hold) so that the rows spread evenly over the CUs in one round, in
+// RTM = ceil(bm / 32) row tiles of 32 (rows of the last tile past bm read as zero and are not
+// written). Every wave computes all RTM row tiles for its columns: the r_pad/32 column tiles of 32 go to the waves round-robin, at most NC per
 // wave, as RTM x NC tiles of v_mfma_f32_32x32x16_bf16. x is read once from HBM, so this is a
 // streaming kernel: K is staged BK (64, or 32 when the A tile is large) at a time through as many LDS
 // stages as fit (up to 8) by buffer->LDS copies of the x tile (RTM*32 x BK), the A tile (r_pad x BK)
@@ -74,15 +75,14 @@ __device__ __forceinline__ u32x4 load_x_chunk(const uint16_t* x, int64_t row, in
   return *reinterpret_cast<const u32x4*>(x + row * K + k);
 }
 
-// bf16(x * pqs) of 8 consecutive elements (pqs values given).
+// bf16(x * pqs) of 8 consecutive elements (pqs values given), rounded by the hardware pair
+// conversion: the bit-level rounding (5 VALU per value) sat on the LoRA-down's critical path.
 __device__ __forceinline__ u32x4 scale_chunk(u32x4 xv, const float (&ps)[8]) {
   u32x4 out;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = bf16_bits_to_f32(xv[i] & 0xffffu) * ps[2 * i];
-    const float hi = bf16_bits_to_f32(xv[i] >> 16) * ps[2 * i + 1];
-    out[i] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-  }
+  for (int i = 0; i < 4; ++i)
+    out[i] = bf16x2_hw(bf16_bits_to_f32(xv[i] & 0xffffu) * ps[2 * i],
+                       __uint_as_float(xv[i] & 0xffff0000u) * ps[2 * i + 1]);
   return out;
 }
 
@@ -165,13 +165,13 @@ template <int RTM, int NC, bool XS>
 __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p) {
   using G = LdGeo<RTM, NC>;
   constexpr int L = G::L, CPT = G::CPT, NS = XS ? G::NS : 0, NST = G::kStages, BK = G::BK;
-  constexpr int BM = RTM * 32;
   static_assert(L <= 7, "wait_tile covers up to 7 tiles in flight");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * p.bm;
+  const int64_t rows = std::min<int64_t>(p.bm, p.S - m0);  // <= 32 * RTM
   const int ct = p.r_pad / 32;  // column tiles: wave w owns tiles w, w + 4, ... (< ct)
 
   LdCtx c;
@@ -182,11 +182,11 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
   c.A_copies = ct * BK / 16;
   c.x_row_bytes = static_cast<uint32_t>(p.K * 2);
   c.A_row_bytes = static_cast<uint32_t>(p.K_pad * 2);
-  c.x = buf_rsrc(p.x + m0 * p.K, static_cast<uint32_t>(std::min<int64_t>(BM, p.S - m0) * p.K * 2));
+  c.x = buf_rsrc(p.x + m0 * p.K, static_cast<uint32_t>(rows * p.K * 2));
   c.A = buf_rsrc(p.A, static_cast<uint32_t>(int64_t{p.r_pad} * p.K_pad * 2));
   c.pq = buf_rsrc(p.pqs, p.pqs ? static_cast<uint32_t>(p.K * 4) : 0u);
   c.xs = buf_rsrc(p.xs_out + m0 * p.K_pad,
-                  XS ? static_cast<uint32_t>(std::min<int64_t>(BM, p.S - m0) * p.K_pad * 2) : 0u);
+                  XS ? static_cast<uint32_t>(rows * p.K_pad * 2) : 0u);
 
   f32x16 acc[RTM][NC];
 #pragma unroll
@@ -229,34 +229,48 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
         for (int j = 0; j < NC; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (XS) {
+    if constexpr (XS) {
       // xs = bf16(x * pqs) of the whole tile from its LDS copy, row-major: chunk q of the workgroup
       // (16 bytes) is row q / (BK/8), chunk q % (BK/8), so one store of a wave covers 8 (BK = 64) or
-      // 16 (BK = 32) rows of full row segments. Every wave issues NS stores; chunks past the tile
-      // go past the buffer's end and are dropped.
+      // 16 (BK = 32) rows of full row segments. A lane's chunks all sit at the same column
+      // (lane % (BK/8)), so its 8 pqs values are read once; all NS chunks are read before the first
+      // store, so the LDS latency is paid once. Every wave issues NS stores; chunks past the tile go
+      // past the buffer's end and are dropped.
+      constexpr bool kAllReal = G::kChunks % 256 == 0;
+      const uint32_t cc = lane % (BK / 8);
+      float ps[8];
+      if (p.pqs) {
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32 + 16);
+        ps[0] = q0.x; ps[1] = q0.y; ps[2] = q0.z; ps[3] = q0.w;
+        ps[4] = q1.x; ps[5] = q1.y; ps[6] = q1.z; ps[7] = q1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ps[e] = 1.0f;
+      }
+      u32x4 xv[NS];
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const uint32_t row = (wave * 64 + lane + 256u * q) / (BK / 8);
+        const bool real = kAllReal || static_cast<int>(wave * 64 + lane + 256u * q) < G::kChunks;
+        xv[q] = real ? *reinterpret_cast<const u32x4*>(st + G::kX + tile_offset<BK>(row, cc)) : u32x4{0u, 0u, 0u, 0u};
+      }
+      if (static_cast<int64_t>(kt + 1) * BK > p.K) {  // the last tile: padding columns become zero
+        const bool pad = static_cast<uint32_t>(kt) * BK + cc * 8 >= p.K;
+#pragma unroll
+        for (int q = 0; q < NS; ++q)
+          if (pad) xv[q] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (pad) ps[e] = 1.0f;
+      }
 #pragma unroll
       for (int q = 0; q < NS; ++q) {
         const uint32_t chunk = wave * 64 + lane + 256u * q;
-        const uint32_t row = chunk / (BK / 8), cc = chunk % (BK / 8);
-        const bool real = static_cast<int>(chunk) < G::kChunks;
-        u32x4 out = u32x4{0u, 0u, 0u, 0u};
-        if (real) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(st + G::kX + tile_offset<BK>(row, cc));
-          float ps[8];
-          if (p.pqs) {
-            const f32x4 q0 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32);
-            const f32x4 q1 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32 + 16);
-            ps[0] = q0.x; ps[1] = q0.y; ps[2] = q0.z; ps[3] = q0.w;
-            ps[4] = q1.x; ps[5] = q1.y; ps[6] = q1.z; ps[7] = q1.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ps[e] = 1.0f;
-          }
-          out = scale_chunk(xv, ps);
-          if (static_cast<uint32_t>(kt) * BK + cc * 8 >= p.K) out = u32x4{0u, 0u, 0u, 0u};  // padding columns
-        }
+        const bool real = kAllReal || static_cast<int>(chunk) < G::kChunks;
+        const u32x4 out = scale_chunk(xv[q], ps);
         // (the dummy offset stays out of range with the tile's column offset added: < 2^31 + 2^21)
-        buf_store16(out, c.xs, real ? row * static_cast<uint32_t>(p.K_pad * 2) + cc * 16 : 0x7ffffff0u,
+        buf_store16(out, c.xs, real ? (chunk / (BK / 8)) * static_cast<uint32_t>(p.K_pad * 2) + cc * 16 : 0x7ffffff0u,
                     static_cast<uint32_t>(kt) * BK * 2);
       }
     }
@@ -271,12 +285,13 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
   for (int i = 0; i < RTM; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = m0 + i * 32 + (r >> 2) * 8 + row_lane + (r & 3);
-      if (row >= p.S) continue;
+      const int64_t rl = i * 32 + (r >> 2) * 8 + row_lane + (r & 3);
+      if (rl >= rows) continue;
+      const int64_t row = m0 + rl;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int jt = static_cast<int>(wave) + 4 * j;
-        if (jt < ct) p.t_out[row * R + jt * 32 + r32] = static_cast<uint16_t>(f32_to_bf16_rne(f * acc[i][j][r]));
+        if (jt < ct) p.t_out[row * R + jt * 32 + r32] = static_cast<uint16_t>(f32_to_bf16_hw(f * acc[i][j][r]));
       }
     }
 }
@@ -343,20 +358,20 @@ hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (cus <= 0) return hipErrorInvalidValue;
-  // rows per workgroup: spread the row tiles of 32 over the CUs in one round (within the register
-  // budget of the column tiles each wave holds)
+  // rows per workgroup: spread the rows evenly over the CUs in one round (at least one row tile of
+  // 32, at most the row tiles whose accumulators fit beside the column tiles each wave holds)
   const int nc = (p.r_pad / 32 + 3) / 4;
-  const int64_t row_tiles = (p.S + 31) / 32;
-  const int rtm = static_cast<int>(
-      std::min<int64_t>(max_rtm(nc), std::max<int64_t>(1, (row_tiles + cus - 1) / cus)));
-  const int64_t blocks = (row_tiles + rtm - 1) / rtm;
+  LoraDownParams q = p;
+  q.bm = std::min<int64_t>(32 * max_rtm(nc), std::max<int64_t>(32, (p.S + cus - 1) / cus));
+  const int rtm = static_cast<int>((q.bm + 31) / 32);
+  const int64_t blocks = (p.S + q.bm - 1) / q.bm;
   switch (rtm) {
-    case 1: return launch_nc<1>(p, nc, blocks, stream);
-    case 2: return launch_nc<2>(p, nc, blocks, stream);
-    case 3: return launch_nc<3>(p, nc, blocks, stream);
-    case 4: return launch_nc<4>(p, nc, blocks, stream);
-    case 5: return launch_nc<5>(p, nc, blocks, stream);
-    default: return launch_nc<6>(p, nc, blocks, stream);
+    case 1: return launch_nc<1>(q, nc, blocks, stream);
+    case 2: return launch_nc<2>(q, nc, blocks, stream);
+    case 3: return launch_nc<3>(q, nc, blocks, stream);
+    case 4: return launch_nc<4>(q, nc, blocks, stream);
+    case 5: return launch_nc<5>(q, nc, blocks, stream);
+    default: return launch_nc<6>(q, nc, blocks, stream);
   }
 }
 

@@ -133,6 +133,8 @@ CASES = [
     (513, 320, 256, 512, 64.0, 0.5, False),
     (100, 512, 2 * 200, 128, 128.0, 1.0, True),
     (70, 96, 2 * 116, 16, 8.0, 1.0, True),       # F not a multiple of 8: the 2-byte store path
+    (9000, 320, 256, 128, 128.0, 1.0, False),    # LoRA-down: 36 rows per workgroup (2 row tiles, 28 rows masked)
+    (9001, 256, 192, 384, 384.0, 1.0, False),    # the same with 3 column tiles per wave (r = 384)
 ]
 
 

@@ -409,6 +409,43 @@ def adaln_curve(stream, device, reps=50):
             "table_flop": 2 * c.blocks * c.samples * c.lora_rank * c.emb_dim}
 
 
+def library_bf16_gemm(projs, S, device, calls=5):
+    """Context, not a product path: torch's bf16 matrix product (the ROCm BLAS library it dispatches
+    to) on each projection's contraction, x [S, K + r] times a dense bf16 weight [K + r, N] (N(0, 1)
+    activations, N(0, 0.02) weights): what a tuned library reaches on the same dense shapes with no
+    4-bit decode and no adapter pass. Per-call time is the mean of `calls` calls after two warm-ups."""
+    import torch
+
+    from bit_linear_dynamic_amd import synth
+
+    out, flop_sum, ms_sum = {}, 0.0, 0.0
+    for i, d in enumerate(projs):
+        p = d["p"]
+        kt = p.K + p.rank
+        x = synth.normal((S, kt), 1.0, synth.seed_of(12, i, 0), device, torch.bfloat16)
+        w = synth.normal((kt, p.N), 0.02, synth.seed_of(12, i, 1), device, torch.bfloat16)
+        y = torch.empty((S, p.N), dtype=torch.bfloat16, device=device)
+        for _ in range(2):
+            torch.mm(x, w, out=y)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(calls):
+            torch.mm(x, w, out=y)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / calls
+        flop = 2.0 * S * p.N * kt
+        out[p.name] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+        flop_sum += flop
+        ms_sum += ms
+        del x, w, y
+    torch.cuda.empty_cache()
+    out["block_tflops"] = round(flop_sum / (ms_sum * 1e-3) / 1e12, 1)
+    out["library"] = str(torch.backends.cuda.preferred_blas_library())
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -504,6 +541,7 @@ def main():
     w4a4 = None if args.timed_only else w4a4_gate_up(projs, stream)
     ceiling = None if args.timed_only else mfma_ceiling(stream, device, achieved)
     small = None if args.timed_only else small_s_graph(device)
+    library = None if args.timed_only else library_bf16_gemm(projs, S, device)
 
     cpu = None
     if not args.no_cpu:
@@ -542,6 +580,7 @@ def main():
         "mlp_producer_fusion": fusion,
         "w4a4_swiglu_gate_up": w4a4,
         "mfma_loop_ceiling": ceiling,
+        "library_bf16_gemm": library,
         "small_s_latency": small,
         "cpu_baseline": cpu,
     }

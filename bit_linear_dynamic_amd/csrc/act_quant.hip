@@ -15,8 +15,8 @@
 //     (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) * d, d = E4M3(s_b) * ts, all exact products; on a tie
 //     the comparison direction picks the neighbour with the even mantissa bit.
 // The same quantizer serves the merged-weight route on an fp32 input (ActQuantParams::xf: v = the
-// input itself). Two passes: a grid-wide amax (rows over workgroups, 16-byte chunks over threads;
-// atomic max on the fp32 bit pattern, exact and order-free), then one thread per 16-element block;
+// input itself). Two passes: a grid-wide amax (blocks of 8 rows over workgroups, 16-byte chunk
+// columns over threads; atomic max on the fp32 bit pattern, exact and order-free), then one thread per 16-element block;
 // without pqs, v = x * 1 = x in both. The second pass can also write the decoded activation
 // E2M1 * E4M3 (exact bf16, tensor scale left to the GEMM epilogue) as the GEMM's operand.
 #include "h3q_device.hpp"
@@ -28,24 +28,36 @@ namespace {
 
 __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 
-// Grid-strided over rows, threads strided over the 16-byte chunks of a row (no division per element).
+// Rows in blocks of kAmaxRows (grid-strided over workgroups); thread t owns the 16-byte chunk
+// columns t, t + 256, ... of a block and loads that column of all the block's rows before reducing
+// them, so it keeps kAmaxRows independent loads in flight and reads its pqs values once per column.
+// (One load per thread at a time, a row at a time, streamed x at ~2 TB/s.)
+constexpr int kAmaxRows = 8;
+
 __global__ __launch_bounds__(256) void amax_kernel(ActQuantParams p) {
   float m = 0.0f;
-  if (p.xf) {  // fp32 input: 4 values per chunk (K % 16 == 0)
-    const int64_t chunks = p.K / 4;
-    for (int64_t row = blockIdx.x; row < p.S; row += gridDim.x) {
-      const f32x4* xr = reinterpret_cast<const f32x4*>(p.xf + row * p.K);
+  const int64_t nblk = (p.S + kAmaxRows - 1) / kAmaxRows;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int64_t r0 = blk * kAmaxRows;
+    const int64_t nr = p.S - r0 < kAmaxRows ? p.S - r0 : kAmaxRows;  // rows of this block
+    if (p.xf) {  // fp32 input: 4 values per chunk (K % 16 == 0)
+      const int64_t chunks = p.K / 4;
       for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
-        const f32x4 v = xr[c];
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        f32x4 v[kAmaxRows];
+#pragma unroll
+        for (int i = 0; i < kAmaxRows; ++i)
+          v[i] = i < nr ? *reinterpret_cast<const f32x4*>(p.xf + (r0 + i) * p.K + c * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kAmaxRows; ++i)
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
       }
-    }
-  } else {  // bf16 input times pqs: 8 values per chunk
-    const int64_t chunks = p.K / 8;
-    for (int64_t row = blockIdx.x; row < p.S; row += gridDim.x) {
-      const u32x4* xr = reinterpret_cast<const u32x4*>(p.x + row * p.K);
+    } else {  // bf16 input times pqs: 8 values per chunk
+      const int64_t chunks = p.K / 8;
       for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
-        const u32x4 v = xr[c];
+        u32x4 v[kAmaxRows];
+#pragma unroll
+        for (int i = 0; i < kAmaxRows; ++i)
+          v[i] = i < nr ? *reinterpret_cast<const u32x4*>(p.x + (r0 + i) * p.K + c * 8) : u32x4{0u, 0u, 0u, 0u};
         float pq[8];
         if (p.pqs) {
           const f32x4 q0 = *reinterpret_cast<const f32x4*>(p.pqs + c * 8);
@@ -56,11 +68,14 @@ __global__ __launch_bounds__(256) void amax_kernel(ActQuantParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) pq[e] = 1.0f;
         }
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] & 0xffffu) * pq[2 * e]));
-          m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] >> 16) * pq[2 * e + 1]));
+        for (int i = 0; i < kAmaxRows; ++i) {
+          const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] & 0xffffu) * pq[2 * e]));
+            m = fmaxf(m, fabsf(__uint_as_float(w[e] & 0xffff0000u) * pq[2 * e + 1]));
+          }
         }
       }
     }
@@ -176,7 +191,8 @@ hipError_t launch_act_quant(const ActQuantParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.S > 0) {
-    const int64_t grid = p.S < 256 * 16 ? p.S : 256 * 16;  // one or more whole rows per workgroup
+    const int64_t blocks = (p.S + kAmaxRows - 1) / kAmaxRows;
+    const int64_t grid = blocks < 256 * 8 ? blocks : 256 * 8;  // one or more row blocks per workgroup
     hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -614,12 +614,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
   c.wave = wave;
   c.lane = lane;
   c.lane16 = lane * 16;
-  c.act = rsrc(p.act, static_cast<uint32_t>(p.S * p.act_ld * 2));
+  // The activation and t' descriptors start at the tile's first row, so every offset stays within
+  // 32 bits whatever S is (rows past S read as zero: the range ends with the tile's last real row).
+  const int64_t tile_rows = min(static_cast<int64_t>(BM), p.S - m0);
+  c.act = rsrc(p.act + m0 * p.act_ld, static_cast<uint32_t>(tile_rows * p.act_ld * 2));
   c.codes = rsrc(p.wcodes + static_cast<int64_t>(nt) * p.k_tiles * kCodeTileBytes,
                  static_cast<uint32_t>(p.k_tiles) * kCodeTileBytes);
   c.scales = rsrc(p.wscales + static_cast<int64_t>(nt) * p.k_tiles * kScaleTileBytes,
                   static_cast<uint32_t>(p.k_tiles) * kScaleTileBytes);
-  c.lt = rsrc(p.lora_t, p.r_tiles ? static_cast<uint32_t>(p.S * p.lora_t_ld * 2) : 0u);
+  c.lt = rsrc(p.r_tiles ? p.lora_t + m0 * p.lora_t_ld : nullptr,
+              p.r_tiles ? static_cast<uint32_t>(tile_rows * p.lora_t_ld * 2) : 0u);
   c.lb = rsrc(reinterpret_cast<const uint8_t*>(p.lora_b) + static_cast<int64_t>(nt) * p.r_tiles * kLoraTileBytes,
               static_cast<uint32_t>(p.r_tiles) * kLoraTileBytes);
 #pragma unroll
@@ -627,13 +631,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4_kernel(GemmParams p) {
     {  // base tile slot (8w + h)*64 + lane -> row, chunk (see Ctx)
       const uint32_t row = (wave * 8 + h) * 8 + (lane >> 3);
       const uint32_t chunk = (lane & 7) ^ ((row >> 1) & 7);
-      c.vact[h] = (static_cast<uint32_t>(m0) + row) * static_cast<uint32_t>(p.act_ld * 2) + chunk * 16;
+      c.vact[h] = row * static_cast<uint32_t>(p.act_ld * 2) + chunk * 16;
     }
     {  // LoRA t' slot (4w + h)*64 + lane -> 128-byte line, then (row, chunk) of the 64-byte rows
       const uint32_t line = (wave * 4 + h) * 8 + (lane >> 3);
       const uint32_t cl = (lane & 7) ^ ((line >> 1) & 7);
       const uint32_t row = line * 2 + (cl >> 2), chunk = cl & 3;
-      c.vlt[h] = (static_cast<uint32_t>(m0) + row) * static_cast<uint32_t>(p.lora_t_ld * 2) + chunk * 16;
+      c.vlt[h] = row * static_cast<uint32_t>(p.lora_t_ld * 2) + chunk * 16;
     }
     {  // LoRA B slot (4w + h)*64 + lane, the same mapping over B's 256 rows
       const uint32_t line = (wave * 4 + h) * 8 + (lane >> 3);

@@ -10,19 +10,19 @@
 // Geometry: one workgroup of 4 wave64s per CU, bm = ceil(S / CUs) rows per workgroup (at least 32,
 // at most what the accumulators hold) so that the rows spread evenly over the CUs in one round, in
 // RTM = ceil(bm / 32) row tiles of 32 (rows of the last tile past bm read as zero and are not
-// written). Every wave computes all RTM row tiles for its columns: the r_pad/32 column tiles of 32 go to the waves round-robin, at most NC per
-// wave, as RTM x NC tiles of v_mfma_f32_32x32x16_bf16. x is read once from HBM, so this is a
-// streaming kernel: K is staged BK (64, or 32 when the A tile is large) at a time through as many LDS
-// stages as fit (up to 8) by buffer->LDS copies of the x tile (RTM*32 x BK), the A tile (r_pad x BK)
-// and BK pqs values, and the
-// global latency is hidden by the bytes in flight rather than by compute. Each wave waits for its
-// own copies with one vmcnt and a barrier hands the stage over. The waves also write
-// xs = bf16(x * pqs), reading the tile back from LDS row by row so that every store covers whole
-// 128-byte row segments (8 rows per store of a wave; stores of 32-byte pieces of 32 rows, straight
-// from the MFMA operand registers, ran the write stream at a fraction of the read rate). Every vector-memory operation of the K loop is issued by the asm helpers of
-// h3q_device.hpp in a fixed number per wave per tile (copies without a real source re-read into a
-// spare LDS area, stores without a real target go past the buffer's end and are dropped), so one
-// vmcnt value per iteration waits exactly for the tile about to be read.
+// written). Every wave computes all RTM row tiles for its columns: the r_pad/32 column tiles of 32
+// go to the waves round-robin, at most NC per wave, as RTM x NC tiles of v_mfma_f32_32x32x16_bf16.
+// x is read once from HBM, so this is a streaming kernel: K is staged BK (64, or 32 when the A tile
+// is large) at a time through as many LDS stages as fit (up to 8) by buffer->LDS copies of the x
+// tile (RTM*32 x BK), the A tile (r_pad x BK) and BK pqs values, and the global latency is hidden by
+// the bytes in flight rather than by compute. Each wave waits for its own copies with one vmcnt and
+// a barrier hands the stage over. The waves also write xs = bf16(x * pqs), reading the tile back
+// from LDS row by row so that every store covers whole 128-byte row segments (8 rows per store of a
+// wave; stores of 32-byte pieces of 32 rows, straight from the MFMA operand registers, ran the write
+// stream at a fraction of the read rate). Every vector-memory operation of the K loop is issued by
+// the asm helpers of h3q_device.hpp in a fixed number per wave per tile (copies without a real
+// source re-read into a spare LDS area, stores without a real target go past the buffer's end and
+// are dropped), so one vmcnt value per iteration waits exactly for the tile about to be read.
 //
 // Prescale: the elementwise xs = bf16(x * pqs) on its own, for calls without an adapter.
 #include <algorithm>

@@ -836,24 +836,14 @@ hipError_t launch_variant(const GemmParams& p0, hipStream_t stream) {
   });
   if (attr_err != hipSuccess) return attr_err;
 
-  // Buffer offsets are 32-bit: launch row ranges whose activation and t' spans stay below 2 GiB.
-  const int64_t row_bytes = std::max<int64_t>(p0.act_ld, p0.lora_t_ld) * 2;
-  const int64_t rows_per_launch = ((int64_t{1} << 31) - 1) / row_bytes / BM * BM;
-  for (int64_t r0 = 0; r0 < p0.S; r0 += rows_per_launch) {
-    GemmParams p = p0;
-    p.S = std::min<int64_t>(rows_per_launch, p0.S - r0);
-    p.act = p0.act + r0 * p0.act_ld;
-    p.lora_t = p0.lora_t ? p0.lora_t + r0 * p0.lora_t_ld : nullptr;
-    p.out = p0.out + r0 * p0.out_ld;
-    if (p.emit_out) p.emit_out = p0.emit_out + r0 * p0.emit_ld;
-    p.m_tiles = static_cast<int32_t>((p.S + BM - 1) / BM);
-    const int64_t items = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
-    const int64_t grid = (items + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_w4_kernel<EPI, LORA>), dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
+  // One launch covers every row: the activation and t' descriptors start at each tile's first row,
+  // so their 32-bit offsets stay within one tile whatever S is.
+  GemmParams p = p0;
+  p.m_tiles = static_cast<int32_t>((p.S + BM - 1) / BM);
+  const int64_t items = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
+  const int64_t grid = (items + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_w4_kernel<EPI, LORA>), dim3(grid), dim3(kThreads), kLdsBytes, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -174,13 +174,13 @@ def test_w4a4_swiglu_gate_up_s37726(block):
 
 
 def test_rows_beyond_32bit_offsets(block):
-    """The down projection (K = 16384) at S = 65836: the activation spans 2.16 GB, more than the
-    GEMM's 32-bit buffer offsets reach, so the call runs as several row ranges. Rows on both sides
-    of each range boundary and the ragged tail match the oracle, and the first rows are bit-identical
-    to a short call's."""
+    """The down projection (K = 16384) at S = 65836: the activation spans 2.16 GB, past what a 32-bit
+    offset from the buffer's start reaches at 2 GiB (the GEMM addresses each tile from its first
+    row). Rows on both sides of each 2 GiB boundary and the ragged tail match the oracle, and the
+    first rows are bit-identical to a short call's."""
     i, p, pr = block["down"]
     S = 65836
-    say(f"S={S} down, row ranges")
+    say(f"S={S} down, past 2 GiB of operand")
     x, pqs = inputs(6, i, S, p.K)
     y = h3q.h3q_linear(x, pqs, pr.handle, 1, 1.0)
     y_short = h3q.h3q_linear(x[:300].contiguous(), pqs, pr.handle, 1, 1.0)

@@ -6,11 +6,17 @@ down 6144x16384 r=128; rank = alpha; strength 1; adapter active), each through h
 (+ x * pqs) and the W4 GEMM with the folded LoRA-up and the epilogue. Inputs are synthetic (seeded),
 resident in HBM before timing starts.
 
-  metric  effective TFLOP/s = sum over projections of 2 S N K + 2 S r (K + N), per second of wall time
-  roofline  the main GEMM kernel (MFMA-bound): 2 S N (K + r) FLOP per launch over its HIP-event time
-  cpu_baseline  the fp64 oracle on a bounded row sample of the same workload, on the host cores
+  metric  effective TFLOP/s = sum over projections of 2 S N K + 2 S r (K + N), per second of wall time;
+          the median of 5 loops of K steps each, with the library's per-kernel timing off
+  roofline  the main GEMM kernel (MFMA-bound): 2 S N (K + r) FLOP per launch over its HIP-event time,
+          from one more loop of K steps with the per-kernel events on
+  cpu_baseline  the fp64 oracle on a fixed row subset of the same workload (the first 256 rows, the
+          last 256 and every 64th), on the host cores, with the full-S time extrapolated
+Side sections time the other workload configurations with the same protocol: the block at S = 8192,
+at S = 37728 (the canvas's second packed length), and adapter switching at S = 16384 (two resident
+adapters x strengths 0, 0.5, 1, and adapter none).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--S 37726] [--cpu-rows R | --no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--loops L] [--S 37726] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -50,8 +56,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--loops", type=int, default=5, help="timed loops of --steps steps; the median is reported")
     ap.add_argument("--S", type=int, default=37726)
-    ap.add_argument("--cpu-rows", type=int, default=384, help="rows per projection in the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--proj", choices=["qkv", "attn_out", "gate_up", "down"], default=None,
                     help="profiling aid: time one projection only (the JSON line then covers only it)")
@@ -63,8 +69,9 @@ def parse():
 
 
 def build_block(S, device, only=None):
-    """Pack the four projections (weights quantized on the device by h3q_quantize_nvfp4 from
-    N(0, 0.02) draws) and register one adapter each; returns per-projection state."""
+    """Pack the four projections (weights quantized on the device by h3q_debug_quantize_act from
+    N(0, 0.02) draws) and register two adapters each (ids 1 and 2: distinct seeds, the projection's
+    rank with alpha = rank); x and y hold S rows (the side sections use row prefixes of them)."""
     import torch
 
     import bit_linear_dynamic_amd as h3q
@@ -77,7 +84,7 @@ def build_block(S, device, only=None):
         if only is not None and p.name != only:
             continue
         w = synth.weight_fp32(p.N, p.K, synth.seed_of(3, i, synth.W), device).to(torch.bfloat16)
-        codes, scales, ts = h3q.h3q_quantize_nvfp4(w)
+        codes, scales, ts = h3q.h3q_debug_quantize_act(w)
         torch.cuda.synchronize()
         del w
         handle = h3q.h3q_pack_weight(codes.cpu(), scales.cpu(), ts.item(), p.N, p.K,
@@ -86,6 +93,9 @@ def build_block(S, device, only=None):
         del codes, scales
         A, B = synth.lora_factors(p.N, p.K, p.rank, synth.seed_of(3, i, synth.A1), synth.seed_of(3, i, synth.B1), device)
         h3q.h3q_register_adapter(handle, 1, A.cpu(), B.cpu(), p.rank, p.alpha)
+        A2, B2 = synth.lora_factors(p.N, p.K, p.rank, synth.seed_of(3, i, synth.A2), synth.seed_of(3, i, synth.B2))
+        h3q.h3q_register_adapter(handle, 2, A2, B2, p.rank, p.alpha)
+        del A2, B2
         if p.K not in xs:
             xs[p.K] = (synth.activation(S, p.K, synth.seed_of(3, i, synth.X), device),
                        synth.pre_quant_scale(p.K, synth.seed_of(3, i, synth.PQS), device))
@@ -96,22 +106,105 @@ def build_block(S, device, only=None):
     return projs
 
 
-def step(projs, stream):
+def step(projs, stream, S, adapter_id=1, strength=1.0):
+    """One block pass: the four projections on the first S rows of x (all rows by default)."""
     import bit_linear_dynamic_amd as h3q
     for d in projs:
-        h3q.h3q_linear(d["x"], d["pqs"], d["handle"], 1, 1.0, y=d["y"], stream=stream)
+        x, y = d["rows"][S]
+        h3q.h3q_linear(x, d["pqs"], d["handle"], adapter_id, strength, y=y, stream=stream)
 
 
-def cpu_baseline(projs, S, rows_per_proj):
-    """The oracle as it stands, on rows_per_proj evenly spaced rows of each projection (incl. the
-    first and the last row), timed with a wall clock around the oracle calls only."""
+def time_loops(run, steps, loops, stream):
+    """Per-step milliseconds of `loops` timed loops of `steps` calls of run(), each loop bracketed by
+    device synchronization and events on `stream`; returns (median, every loop's value)."""
+    import torch
+    per = []
+    for _ in range(loops):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / steps)
+    return sorted(per)[len(per) // 2], [round(v, 4) for v in per]
+
+
+def block_side(projs, stream, S, steps, loops):
+    """The block at another sequence length (a row prefix of the same inputs), same protocol."""
+    from bit_linear_dynamic_amd import workloads as wl
+    step(projs, stream, S)
+    ms, per = time_loops(lambda: step(projs, stream, S), steps, loops, stream)
+    flops = sum(wl.effective_flops(S, d["p"]) for d in projs)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"S": S, "ms_per_step": round(ms, 4), "loops_ms_per_step": per, "effective_tflops": round(tf, 1),
+            "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "tflop_per_step": round(flops / 1e12, 4)}
+
+
+def switching(projs, stream, S, steps, loops):
+    """Adapter switching at S: per block pass (four projections), every (adapter, strength) pair of
+    {none, 1, 2} x {0, 0.5, 1}, and a pass that alternates adapters 1 and 2 from call to call; a
+    switch is a host-side lookup, so the alternating pass costs what the single-adapter ones do and
+    adapter none or strength 0 costs the base-only call."""
+    from bit_linear_dynamic_amd import workloads as wl
+    import bit_linear_dynamic_amd as h3q
+
+    per_call = {}
+    for aid in (h3q.H3Q_ADAPTER_NONE, 1, 2):
+        for st in (0.0, 0.5, 1.0):
+            step(projs, stream, S, aid, st)
+            ms, _ = time_loops(lambda: step(projs, stream, S, aid, st), steps, loops, stream)
+            per_call[f"{'none' if aid < 0 else aid}@{st}"] = round(ms, 4)
+    flip = [0]
+
+    def alternating():
+        for d in projs:
+            x, y = d["rows"][S]
+            flip[0] ^= 1
+            h3q.h3q_linear(x, d["pqs"], d["handle"], 1 + flip[0], 1.0, y=y, stream=stream)
+
+    alt, _ = time_loops(alternating, steps, loops, stream)
+    active = [per_call[k] for k in ("1@0.5", "1@1.0", "2@0.5", "2@1.0")]
+    base = [per_call[k] for k in ("none@0.0", "none@0.5", "none@1.0", "1@0.0", "2@0.0")]
+    same = (per_call["1@1.0"] + per_call["2@1.0"]) / 2
+    flops_a = sum(wl.effective_flops(S, d["p"]) for d in projs)
+    return {"S": S, "block_ms_per_pass": per_call, "alternating_1_2_ms": round(alt, 4),
+            "switch_overhead_pct": round(100 * (alt - same) / same, 2),
+            "adapter_spread_pct": round(100 * (max(active) - min(active)) / min(active), 2),
+            "base_spread_pct": round(100 * (max(base) - min(base)) / min(base), 2),
+            "adapter_cost_pct": round(100 * (same - min(base)) / min(base), 2),
+            "effective_tflops_adapter": round(flops_a / (same * 1e-3) / 1e12, 1)}
+
+
+def subset_rows(S):
+    """The oracle's fixed row subset: the first 256 rows, the last 256 (holding the ragged last row
+    tile) and every 64th row."""
+    import numpy as np
+    return np.unique(np.concatenate([np.arange(min(256, S)), np.arange(max(0, S - 256), S), np.arange(0, S, 64)]))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(projs, S):
+    """The oracle as it stands, on the row subset of each projection, timed with a wall clock
+    around the oracle calls only; the full-S time is extrapolated from it (rows are independent)."""
     import numpy as np
 
     import oracle
     from bit_linear_dynamic_amd import synth
     from bit_linear_dynamic_amd import workloads as wl
 
-    rows = np.unique(np.linspace(0, S - 1, rows_per_proj).astype(np.int64))
+    rows = subset_rows(S)
     lib = oracle.load()
     inputs = []
     for d in projs:
@@ -127,13 +220,16 @@ def cpu_baseline(projs, S, rows_per_proj):
     dt = time.perf_counter() - t0
     flops = sum(wl.effective_flops(len(rows), p) for *_, p in inputs)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib), "kind": "oracle",
-            "sample": f"{len(rows)} evenly spaced rows (first and last included) of each of the 4 projections "
-                      f"at S={S}, adapter active; {dt:.1f} s wall for {flops / 1e9:.1f} GFLOP effective "
-                      f"(whole-weight fp64 decode per projection included)",
-            "seconds": dt}
+            "sample": f"row subset R of S={S} (the first 256 rows, the last 256, every 64th: {len(rows)} rows) "
+                      f"through each of the 4 projections, adapter 1 at strength 1; {dt:.1f} s wall for "
+                      f"{flops / 1e9:.1f} GFLOP effective (each projection's whole-weight fp64 decode included)",
+            "seconds": round(dt, 3), "rows": int(len(rows)), "block_rows_per_s": round(len(rows) / dt, 2),
+            "extrapolated_full_s": round(dt * S / len(rows), 1),
+            "extrapolated_note": "extrapolated, not measured: the subset's time scaled by S / rows",
+            "cpu_model": cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
-def merged_vs_dynamic(projs, stream, calls=5):
+def merged_vs_dynamic(projs, stream, S, calls=5):
     """Per projection: the dynamic call (LoRA-down + GEMM over K + r_pad) against a base-only call on
     the weight with the update merged in before quantizing (h3q_merge_adapter, then packed), both with
     pqs; plus what one merge costs (device merge + quantize, synchronous) and the host-side pack. The
@@ -166,10 +262,10 @@ def merged_vs_dynamic(projs, stream, calls=5):
                                  h3q.H3Q_PACK_GATE_UP if p.gate_up else 0)
         pack_ms = (time.perf_counter() - t0) * 1e3
         del codes, scales
+        x, y = d["rows"][S]
         try:
-            dyn = per_call_ms(lambda: h3q.h3q_linear(d["x"], d["pqs"], d["handle"], 1, 1.0, y=d["y"], stream=stream))
-            mrg = per_call_ms(lambda: h3q.h3q_linear(d["x"], d["pqs"], mh, h3q.H3Q_ADAPTER_NONE, 0.0, y=d["y"],
-                                                     stream=stream))
+            dyn = per_call_ms(lambda: h3q.h3q_linear(x, d["pqs"], d["handle"], 1, 1.0, y=y, stream=stream))
+            mrg = per_call_ms(lambda: h3q.h3q_linear(x, d["pqs"], mh, h3q.H3Q_ADAPTER_NONE, 0.0, y=y, stream=stream))
         finally:
             h3q.h3q_free_weight(mh)
         out[p.name] = {"dynamic_ms": round(dyn, 4), "merged_ms": round(mrg, 4),
@@ -182,7 +278,7 @@ def merged_vs_dynamic(projs, stream, calls=5):
     return out
 
 
-def producer_fusion(projs, stream, calls=5):
+def producer_fusion(projs, stream, S, calls=5):
     """The MLP pair gate/up -> down per call, unfused (SwiGLU writes h; the down call makes its own
     base operand bf16(h * pqs) in LoRA-down or the prescale pass) against fused (the SwiGLU epilogue
     also writes that operand; the down call takes it as given), with adapter 1 at strength 1 and with
@@ -195,18 +291,19 @@ def producer_fusion(projs, stream, calls=5):
     if "gate_up" not in by or "down" not in by:
         return None
     gu, dn = by["gate_up"], by["down"]
-    S, F = gu["x"].shape[0], gu["p"].N // 2
-    h = torch.empty((S, F), dtype=torch.bfloat16, device=gu["x"].device)
+    F = gu["p"].N // 2
+    gx, dy = gu["rows"][S][0], dn["rows"][S][1]
+    h = torch.empty((S, F), dtype=torch.bfloat16, device=gx.device)
     xs = torch.empty_like(h)
 
     def unfused(aid, st):
-        h3q.h3q_linear_swiglu(gu["x"], gu["pqs"], gu["handle"], aid, st, h=h, stream=stream)
-        h3q.h3q_linear(h, dn["pqs"], dn["handle"], aid, st, y=dn["y"], stream=stream)
+        h3q.h3q_linear_swiglu(gx, gu["pqs"], gu["handle"], aid, st, h=h, stream=stream)
+        h3q.h3q_linear(h, dn["pqs"], dn["handle"], aid, st, y=dy, stream=stream)
 
     def fused(aid, st):
-        h3q.h3q_linear_swiglu_emit(gu["x"], gu["pqs"], gu["handle"], aid, st, dn["pqs"], h=h, xs_next=xs,
+        h3q.h3q_linear_swiglu_emit(gx, gu["pqs"], gu["handle"], aid, st, dn["pqs"], h=h, xs_next=xs,
                                    stream=stream)
-        h3q.h3q_linear_prescaled(h, xs, dn["handle"], aid, st, y=dn["y"], stream=stream)
+        h3q.h3q_linear_prescaled(h, xs, dn["handle"], aid, st, y=dy, stream=stream)
 
     def per_call_ms(fn, aid, st):
         fn(aid, st)
@@ -229,7 +326,7 @@ def producer_fusion(projs, stream, calls=5):
     return out
 
 
-def w4a4_gate_up(projs, stream, calls=5):
+def w4a4_gate_up(projs, stream, S, calls=5):
     """The W4A4 variant on the fused gate/up projection at the bench's S: activations quantized to
     NVFP4 per call for the base GEMM, LoRA on the original x, SiLU(gate) * up in the epilogue. Per
     call: wall time, and each kernel's share from the library's HIP events (the quantizer's two passes
@@ -243,12 +340,12 @@ def w4a4_gate_up(projs, stream, calls=5):
     if d is None:
         return None
     p = d["p"]
-    S = d["x"].shape[0]
-    h = torch.empty((S, p.N // 2), dtype=torch.bfloat16, device=d["x"].device)
+    x = d["rows"][S][0]
+    h = torch.empty((S, p.N // 2), dtype=torch.bfloat16, device=x.device)
     flags = h3q.H3Q_ACT_NVFP4 | h3q.H3Q_EPI_SWIGLU
 
     def call():
-        h3q.h3q_linear_ex(d["x"], d["pqs"], d["handle"], 1, 1.0, flags, out=h, stream=stream)
+        h3q.h3q_linear_ex(x, d["pqs"], d["handle"], 1, 1.0, flags, out=h, stream=stream)
 
     call()
     torch.cuda.synchronize()
@@ -286,7 +383,7 @@ def small_s_graph(device, calls=20, replays=10):
 
     p, S = wl.SMALL_QKV, wl.S_SMALL
     w = synth.weight_fp32(p.N, p.K, synth.seed_of(1, 0, synth.W), device).to(torch.bfloat16)
-    codes, scales, ts = h3q.h3q_quantize_nvfp4(w)
+    codes, scales, ts = h3q.h3q_debug_quantize_act(w)
     torch.cuda.synchronize()
     handle = h3q.h3q_pack_weight(codes.cpu(), scales.cpu(), ts.item(), p.N, p.K)
     try:
@@ -468,29 +565,33 @@ def main():
         print(json.dumps({"calibrate_copy_mib": args.calibrate_copy, "launches": 3}), flush=True)
         return
     S = args.S
+    # the side sections: the block at S = 8192 and at S + 2 = 37728 (the canvas's second packed length,
+    # whose first 37726 rows are the headline's input), and adapter switching at S = 16384
+    side = not args.timed_only and S == wl.S_CANVAS
+    S_alloc = wl.S_CANVAS_ALT if side else S
     print(f"bench: building the projections at S={S}", file=sys.stderr, flush=True)
-    projs = build_block(S, device, args.proj)
+    projs = build_block(S_alloc, device, args.proj)
+    for d in projs:
+        d["rows"] = {n: (d["x"][:n], d["y"][:n]) for n in {S, S_alloc, wl.S_MID, wl.S_SWITCH} if n <= S_alloc}
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
-        step(projs, stream)
+        step(projs, stream, S)
     torch.cuda.synchronize()
-    print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"bench: warmup done, timing {args.loops} loops of {args.steps} steps", file=sys.stderr, flush=True)
 
+    # headline: the median of the loops, nothing but the library's own launches on the stream
+    ms_per_step, loops_ms = time_loops(lambda: step(projs, stream, S), args.steps, args.loops, stream)
+
+    # per-kernel breakdown: one more loop with the library's HIP events around each launch
     h3q.h3q_timing_enable(True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
     for _ in range(args.steps):
-        step(projs, stream)
-    end.record(stream)
+        step(projs, stream, S)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
     gemm_ms, gemm_n = h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM)
     down_ms, down_n = h3q.h3q_timing_get(h3q.H3Q_KERNEL_LORA_DOWN)
     h3q.h3q_timing_enable(False)
 
-    ms_per_step = total_ms / args.steps
     flops_step = sum(wl.effective_flops(S, d["p"]) for d in projs)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     gemm_flops_launch = sum(2 * S * d["p"].N * (d["p"].K + d["p"].rank) for d in projs) / len(projs)
@@ -501,8 +602,9 @@ def main():
     per_proj = {}
     for d in ([] if args.timed_only else projs):
         h3q.h3q_timing_enable(True)
+        x, y = d["rows"][S]
         for _ in range(3):
-            h3q.h3q_linear(d["x"], d["pqs"], d["handle"], 1, 1.0, y=d["y"])
+            h3q.h3q_linear(x, d["pqs"], d["handle"], 1, 1.0, y=y)
         torch.cuda.synchronize()
         g, gn = h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM)
         l, ln = h3q.h3q_timing_get(h3q.H3Q_KERNEL_LORA_DOWN)
@@ -521,12 +623,12 @@ def main():
         q_width = p.N // 3
         g = torch.ones(q_width, dtype=torch.float32, device=device)
         cos, sin = (t.to(device) for t in synth.rope_table(S, 96))
-        h3q.h3q_linear_qk_norm_rope(d["x"], d["pqs"], d["handle"], 1, 1.0, q_width, 96, 1e-6, g, g, cos, sin, y=d["y"])
+        x, y = d["rows"][S]
+        h3q.h3q_linear_qk_norm_rope(x, d["pqs"], d["handle"], 1, 1.0, q_width, 96, 1e-6, g, g, cos, sin, y=y)
         torch.cuda.synchronize()
         h3q.h3q_timing_enable(True)
         for _ in range(3):
-            h3q.h3q_linear_qk_norm_rope(d["x"], d["pqs"], d["handle"], 1, 1.0, q_width, 96, 1e-6, g, g, cos, sin,
-                                        y=d["y"])
+            h3q.h3q_linear_qk_norm_rope(x, d["pqs"], d["handle"], 1, 1.0, q_width, 96, 1e-6, g, g, cos, sin, y=y)
         torch.cuda.synchronize()
         gq, gqn = h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM)
         h3q.h3q_timing_enable(False)
@@ -534,11 +636,16 @@ def main():
         qk = {"gemm_ms": round(gq / gqn, 4), "plain_gemm_ms": plain,
               "epilogue_overhead_pct": round(100.0 * (gq / gqn - plain) / plain, 2)}
 
+    # the other workload configurations, same protocol
+    cfg2 = block_side(projs, stream, wl.S_MID, args.steps, args.loops) if side else None
+    cfg3alt = block_side(projs, stream, wl.S_CANVAS_ALT, args.steps, args.loops) if side else None
+    cfg4 = switching(projs, stream, wl.S_SWITCH, max(1, args.steps // 2), args.loops) if side else None
+
     # the merged route (the update folded into the weight before quantizing) against the dynamic call
-    mvd = None if args.timed_only else merged_vs_dynamic(projs, stream)
+    mvd = None if args.timed_only else merged_vs_dynamic(projs, stream, S)
     adaln = None if args.timed_only else adaln_curve(stream, device)
-    fusion = None if args.timed_only else producer_fusion(projs, stream)
-    w4a4 = None if args.timed_only else w4a4_gate_up(projs, stream)
+    fusion = None if args.timed_only else producer_fusion(projs, stream, S)
+    w4a4 = None if args.timed_only else w4a4_gate_up(projs, stream, S)
     ceiling = None if args.timed_only else mfma_ceiling(stream, device, achieved)
     small = None if args.timed_only else small_s_graph(device)
     library = None if args.timed_only else library_bf16_gemm(projs, S, device)
@@ -546,7 +653,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(projs, S, args.cpu_rows)
+        cpu = cpu_baseline(projs, S)
 
     line = {
         "metric": "effective TFLOP/s (+% bf16 MFMA peak) of W4+LoRA linear, S=37726",
@@ -557,6 +664,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "loops": args.loops,
+        "loops_ms_per_step": loops_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -572,7 +681,11 @@ def main():
                      "avg_launch_ms": round(gemm_avg_ms, 4), "launches": gemm_n,
                      "flop_per_launch": gemm_flops_launch, "traffic": gemm_traffic(),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE)"},
-        "kernels_ms_per_step": {"gemm": round(gemm_ms / args.steps, 4), "lora_down": round(down_ms / args.steps, 4)},
+        "kernels_ms_per_step": {"gemm": round(gemm_ms / args.steps, 4), "lora_down": round(down_ms / args.steps, 4),
+                                "note": "from one extra loop of the same steps with per-launch HIP events"},
+        "cfg2_block_s8192": cfg2,
+        "cfg3alt_s37728": cfg3alt,
+        "cfg4_switching_s16384": cfg4,
         "per_projection": per_proj,
         "qkv_with_qk_norm_rope": qk,
         "merged_vs_dynamic": mvd,

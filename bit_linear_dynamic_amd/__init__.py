@@ -50,6 +50,7 @@ def _declare(lib):
         "h3q_linear_ex": [vp, vp, i64, vp, vp, i32, f32, u32, vp],
         "h3q_linear_qk_norm_rope": [vp, vp, i64, vp, vp, i32, f32, u32, i64, i32, f32, vp, vp, vp, vp, vp],
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
+        "h3q_debug_quantize_act": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_dequant": [vp, vp, vp],
         "h3q_merge_adapter": [vp, vp, i32, f32, vp, vp, vp, vp, vp],
         "h3q_mfma_loop": [vp, vp, vp, i32, i32, vp],
@@ -338,17 +339,26 @@ def h3q_mfma_loop(ops_a, ops_b, iters: int, workgroups: int, sink=None, stream=N
     return sink
 
 
-def h3q_quantize_nvfp4(x, pqs=None, stream=None):
-    """Device bf16 x [S][K] -> (codes u8 [S][K/2], scales u8 [S][K/16], ts fp32 [1]) on the device."""
+def _quantize_act(fn, x, pqs, stream):
     import torch
     S, K = x.shape
     codes = torch.empty((S, K // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((S, K // 16), dtype=torch.uint8, device=x.device)
     ts = torch.empty((1,), dtype=torch.float32, device=x.device)
-    _check(lib().h3q_quantize_nvfp4(_stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S, K,
-                                    _dev_ptr(pqs, torch.float32, "pqs"), _dev_ptr(codes), _dev_ptr(scales),
-                                    _dev_ptr(ts)))
+    _check(fn(_stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S, K, _dev_ptr(pqs, torch.float32, "pqs"),
+              _dev_ptr(codes), _dev_ptr(scales), _dev_ptr(ts)))
     return codes, scales, ts
+
+
+def h3q_debug_quantize_act(x, pqs=None, stream=None):
+    """Device bf16 x [S][K] -> (codes u8 [S][K/2], scales u8 [S][K/16], ts fp32 [1]) on the device:
+    the W4A4 activation quantizer exactly as the linear runs it."""
+    return _quantize_act(lib().h3q_debug_quantize_act, x, pqs, stream)
+
+
+def h3q_quantize_nvfp4(x, pqs=None, stream=None):
+    """The same quantizer under its earlier name (kept as an alias)."""
+    return _quantize_act(lib().h3q_quantize_nvfp4, x, pqs, stream)
 
 
 def h3q_debug_dequant(w: int, out=None, stream=None):

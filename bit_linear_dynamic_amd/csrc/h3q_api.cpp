@@ -204,6 +204,10 @@ h3q_status workspace(int dev, hipStream_t stream, size_t need, uint8_t** out) {
     ws.bytes = bytes;
   }
   if (capturing) ws.captured = true;
+  // test hook: while H3Q_TEST_POISON_WORKSPACE is set, every call outside a capture first fills the
+  // part of the workspace it uses with all-ones bytes (bf16 NaN), so that a kernel reading a part
+  // that the call did not write shows up in the output
+  if (!capturing && std::getenv("H3Q_TEST_POISON_WORKSPACE")) H3Q_HIP_TRY(hipMemsetAsync(ws.buf, 0xFF, need, stream));
   *out = static_cast<uint8_t*>(ws.buf);
   return H3Q_OK;
 }
@@ -371,7 +375,7 @@ h3q_status h3q_register_adapter(h3q_weight w, int32_t id, const uint16_t* A, con
 
   Adapter a;
   a.rank = rank;
-  a.r_pad = static_cast<int32_t>(round_up(rank, 64));
+  a.r_pad = static_cast<int32_t>(round_up(rank, kLoraBK));  // whole 32-deep LoRA K-tiles of the GEMM
   a.alpha = alpha;
   const int64_t K = w->K, Kp = w->K_pad, N = w->N;
   std::vector<uint16_t> Ah(static_cast<size_t>(a.r_pad * Kp), 0);
@@ -625,14 +629,14 @@ h3q_status h3q_linear_swiglu(void* stream, const uint16_t* x, int64_t S, const f
   return h3q_linear_ex(stream, x, S, pqs, w, adapter_id, strength, H3Q_EPI_SWIGLU, h);
 }
 
-h3q_status h3q_quantize_nvfp4(void* stream_, const uint16_t* x, int64_t S, int64_t K, const float* pqs,
-                              uint8_t* codes, uint8_t* scales, float* ts) {
+h3q_status h3q_debug_quantize_act(void* stream_, const uint16_t* x, int64_t S, int64_t K, const float* pqs,
+                                  uint8_t* codes, uint8_t* scales, float* ts) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  if (!x || !codes || !scales || !ts) return fail(H3Q_E_ARG, "quantize_nvfp4: null pointer");
+  if (!x || !codes || !scales || !ts) return fail(H3Q_E_ARG, "quantize_act: null pointer");
   if (S < 0 || S > kMaxS || K < 16 || K > kMaxDim || K % 16 != 0)
-    return fail(H3Q_E_SHAPE, "quantize_nvfp4: need 0 <= S <= 2^24, 16 <= K <= 2^20, K %% 16 == 0");
+    return fail(H3Q_E_SHAPE, "quantize_act: need 0 <= S <= 2^24, 16 <= K <= 2^20, K %% 16 == 0");
   if (!aligned16(x) || (pqs && !aligned16(pqs)) || (reinterpret_cast<uintptr_t>(codes) & 7u))
-    return fail(H3Q_E_ARG, "quantize_nvfp4: x, pqs must be 16-byte and codes 8-byte aligned");
+    return fail(H3Q_E_ARG, "quantize_act: x, pqs must be 16-byte and codes 8-byte aligned");
   int dev;
   if (h3q_status st = check_device(&dev)) return st;
   uint8_t* ws = nullptr;
@@ -641,6 +645,11 @@ h3q_status h3q_quantize_nvfp4(void* stream_, const uint16_t* x, int64_t S, int64
   hipError_t e = timed(H3Q_KERNEL_ACT_QUANT, stream, [&] { return launch_act_quant(q, stream); });
   if (e != hipSuccess) return fail(H3Q_E_HIP, "act-quant launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+h3q_status h3q_quantize_nvfp4(void* stream, const uint16_t* x, int64_t S, int64_t K, const float* pqs,
+                              uint8_t* codes, uint8_t* scales, float* ts) {
+  return h3q_debug_quantize_act(stream, x, S, K, pqs, codes, scales, ts);
 }
 
 h3q_status h3q_debug_dequant(void* stream, h3q_weight w, uint16_t* wq) {

@@ -109,6 +109,19 @@ __device__ __forceinline__ uint32_t copy_src_offset(uint32_t q, uint32_t lane, u
   else return (line * 2 + (cl >> 2)) * row_bytes + (cl & 3) * 16;
 }
 
+// Column within the tile (0 .. BK - 8) of the 16 bytes that copy q brings to this lane's slot.
+template <int BK>
+__device__ __forceinline__ uint32_t copy_src_column(uint32_t q, uint32_t lane) {
+  const uint32_t line = q * 8 + (lane >> 3);
+  const uint32_t cl = (lane & 7) ^ ((line >> 1) & 7);
+  if constexpr (BK == 64) return cl * 8;
+  else return (cl & 3) * 8;
+}
+
+// A per-lane offset past the end of the x descriptor (which spans under 2^31 bytes): the copy reads
+// zeros. Adding the tile's column offset (under 2^21 bytes) cannot wrap it past 2^32.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 template <int BK>
 __device__ __forceinline__ uint32_t tile_offset(uint32_t row, uint32_t chunk) {
   if constexpr (BK == 64) return lds_chunk_offset(row, chunk);
@@ -118,6 +131,7 @@ __device__ __forceinline__ uint32_t tile_offset(uint32_t row, uint32_t chunk) {
 struct LdCtx {
   u32x4 x, A, pq, xs;
   uint32_t x_row_bytes, A_row_bytes;
+  uint32_t K;
   uint32_t wave, lane;
   int k_tiles, x_copies, A_copies;  // real copies per tile for the whole workgroup
 };
@@ -132,8 +146,12 @@ __device__ __forceinline__ void issue_tile(const LdCtx& c, int kt, uint32_t stag
   for (int i = 0; i < G::kCopiesX; ++i) {
     const uint32_t q = c.wave + 4 * i;
     const bool real = static_cast<int>(q) < c.x_copies;
-    dma16(c.x, stage + (real ? G::kX + q * 1024 : G::kSpare), copy_src_offset<BK>(real ? q : 0, c.lane, c.x_row_bytes),
-          k0 * 2);
+    const uint32_t qs = real ? q : 0;
+    // x rows are K elements apart, so the 16 bytes past a row's end are the next row's first
+    // elements: columns at or past K read as zero instead (A is zero there, but 0 * inf is not 0).
+    const uint32_t voff = k0 + copy_src_column<BK>(qs, c.lane) < c.K ? copy_src_offset<BK>(qs, c.lane, c.x_row_bytes)
+                                                                    : kOutOfRange;
+    dma16(c.x, stage + (real ? G::kX + q * 1024 : G::kSpare), voff, k0 * 2);
   }
 #pragma unroll
   for (int i = 0; i < G::kCopiesA; ++i) {
@@ -177,7 +195,11 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
   LdCtx c;
   c.wave = wave;
   c.lane = lane;
-  c.k_tiles = static_cast<int>((p.K + BK - 1) / BK);
+  // K_pad / BK tiles (K_pad is a multiple of 64): with 32-deep tiles that can be one tile past
+  // ceil(K / BK), whose x columns are all padding, so xs is written with zeros out to K_pad -- the
+  // GEMM reads K_pad columns of it, and the workspace holds whatever an earlier call left there.
+  c.k_tiles = static_cast<int>(p.K_pad / BK);
+  c.K = static_cast<uint32_t>(p.K);
   c.x_copies = RTM * BK / 16;
   c.A_copies = ct * BK / 16;
   c.x_row_bytes = static_cast<uint32_t>(p.K * 2);
@@ -352,7 +374,7 @@ hipError_t launch_nc(const LoraDownParams& p, int nc, int64_t blocks, hipStream_
 
 hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream) {
   if (p.S == 0) return hipSuccess;
-  if (p.r_pad <= 0 || p.r_pad % 64 != 0 || p.r_pad > 512) return hipErrorInvalidValue;
+  if (p.r_pad <= 0 || p.r_pad % 32 != 0 || p.r_pad > 512) return hipErrorInvalidValue;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -1,5 +1,9 @@
 /* h3q.h -- C ABI of the MI355X (gfx950) W4 + dynamic LoRA linear.
  *
+ * Each entry point below either cites the passage of the pages that defines what it computes, or
+ * says that it is a library convention (handles, introspection, diagnostics, timing), which the
+ * pages do not describe.
+ *
  * The operation (FL2VA Turbo page, section "Implementation"):
  *
  *     y = NVFP4_base(x (*) pre_quant_scale) + strength * (alpha / rank) * B(A x)
@@ -22,8 +26,13 @@
  *   - bf16 tensors are passed as uint16_t bit patterns; all 2-D arrays are row-major and dense.
  *   - "host" pointers are read before the call returns; "device" pointers must stay valid until
  *     the work enqueued on `stream` (a hipStream_t; NULL = the null stream) has run.
- *   - every call returns H3Q_OK (0) or a positive H3Q_E_* code; on error nothing has been enqueued,
- *     no output has been written, and h3q_last_error() describes the failure.
+ *   - every call returns H3Q_OK (0) or a positive H3Q_E_* code and on error sets h3q_last_error().
+ *     Arguments, shapes, formats, adapter ids, the device and the workspace are all checked before
+ *     the first launch, so every code except H3Q_E_HIP means that nothing has been enqueued and no
+ *     output has been written. H3Q_E_HIP reports a launch that the runtime refused: the kernels of
+ *     the same call enqueued before it may still run, but they write only the library's own
+ *     workspace and temporaries (and, for h3q_merge_adapter, its `merged` output), never the
+ *     caller's other outputs, which each call writes in its last kernel.
  *   - a weight handle belongs to the device that was current when it was packed; calls that use it
  *     must be made with that device current.
  *   - calls on different streams may run concurrently; registering or unregistering an adapter
@@ -84,7 +93,8 @@ enum {
 h3q_status h3q_pack_weight(void* stream, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
                            int64_t N, int64_t K, uint32_t flags, h3q_weight* out);
 
-/* Release a handle and every adapter registered on it (no call using it may be in flight). */
+/* Release a handle and every adapter registered on it (no call using it may be in flight).
+ * Library convention (handle lifetime), not on the pages. */
 h3q_status h3q_free_weight(h3q_weight w);
 
 /* Register a resident LoRA adapter on one projection (FL2VA Turbo, "Implementation": A, B, rank and
@@ -95,13 +105,16 @@ h3q_status h3q_free_weight(h3q_weight w);
 h3q_status h3q_register_adapter(h3q_weight w, int32_t id, const uint16_t* A, const uint16_t* B, int32_t rank,
                                 float alpha);
 
-/* Drop an adapter (E_ADAPTER if unknown). No call using it may be in flight. */
+/* Drop an adapter (E_ADAPTER if unknown). No call using it may be in flight. Library convention
+ * (the pages register adapters at start-up and never unload them). */
 h3q_status h3q_unregister_adapter(h3q_weight w, int32_t id);
 
-/* Registered ids of a handle: writes up to `cap` ids to `ids` (host) and the total to *count. */
+/* Registered ids of a handle: writes up to `cap` ids to `ids` (host) and the total to *count.
+ * Library convention (introspection), not on the pages. */
 h3q_status h3q_list_adapters(h3q_weight w, int32_t* ids, int32_t cap, int32_t* count);
 
-/* Dimensions and flags of a handle (any out-pointer may be NULL). */
+/* Dimensions and flags of a handle (any out-pointer may be NULL). Library convention
+ * (introspection), not on the pages. */
 h3q_status h3q_weight_info(h3q_weight w, int64_t* N, int64_t* K, uint32_t* flags);
 
 /* The projection (FL2VA Turbo, "Implementation"):
@@ -119,8 +132,10 @@ h3q_status h3q_linear(void* stream, const uint16_t* x, int64_t S, const float* p
 h3q_status h3q_linear_swiglu(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
                              int32_t adapter_id, float strength, uint16_t* h);
 
-/* h3q_linear with flags (H3Q_ACT_NVFP4, H3Q_EPI_SWIGLU). out is [S][N] or, with H3Q_EPI_SWIGLU,
- * [S][N/2]. With H3Q_ACT_NVFP4 the LoRA branch still receives the original bf16 x. */
+/* h3q_linear with flags (H3Q_ACT_NVFP4, H3Q_EPI_SWIGLU): the projection of FL2VA Turbo,
+ * "Implementation", with the activation quantized to NVFP4 per call for the base path (MiniMax-H3
+ * Ultra Fast, "Kernel path", item 1) and/or the SiLU(gate) * up output. out is [S][N] or, with
+ * H3Q_EPI_SWIGLU, [S][N/2]. With H3Q_ACT_NVFP4 the LoRA branch still receives the original bf16 x. */
 h3q_status h3q_linear_ex(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
                          int32_t adapter_id, float strength, uint32_t flags, uint16_t* out);
 
@@ -215,7 +230,7 @@ h3q_status h3q_adaln_table(void* stream, const float* u, const float* emb, const
 h3q_status h3q_adaln_apply(void* stream, const uint16_t* M, const float* bias, const float* table, const float* t,
                            int32_t T, int32_t blocks, int64_t rows, int32_t samples, int32_t R, float* out);
 
-/* Measurement aid: the matrix-core throughput the board sustains under its power limit, beside which
+/* Measurement aid (library convention, not on the pages): the matrix-core throughput the board sustains under its power limit, beside which
  * the GEMM's rate is read (the nominal dense bf16 peak assumes the full engine clock). Each of the
  * `workgroups` workgroups of 256 threads (two waves per SIMD, as the main GEMM runs) performs
  * iters x 64 v_mfma_f32_32x32x16_bf16 per wave (32768 flops each) on 8 rotating operand pairs, with no
@@ -225,8 +240,9 @@ h3q_status h3q_adaln_apply(void* stream, const uint16_t* M, const float* bias, c
 h3q_status h3q_mfma_loop(void* stream, const uint16_t* ops_a, const uint16_t* ops_b, int32_t iters,
                          int32_t workgroups, float* sink);
 
-/* The W4A4 activation quantizer on its own (MiniMax-H3 Ultra Fast, "Kernel path", item 1), as
- * h3q_linear_ex(H3Q_ACT_NVFP4) runs it:
+/* The W4A4 activation quantizer on its own (MiniMax-H3 Ultra Fast, "Kernel path", item 1: the
+ * activations are quantized to NVFP4 on every call), as h3q_linear_ex(H3Q_ACT_NVFP4) runs it
+ * (the same kernels):
  *   v      = f32(x) * pqs[k] rounded to fp32            (pqs NULL -> v = x)
  *   ts     = amax|v| / (6 * 448) rounded to fp32         (1 when v is all zero)
  *   scale  = E4M3 nearest to amax_block|v| / (6 * ts), ties to even, saturating at 448
@@ -234,25 +250,33 @@ h3q_status h3q_mfma_loop(void* stream, const uint16_t* ops_a, const uint16_t* op
  * Each quotient is the exact quotient rounded once. All pointers are device pointers:
  *   x bf16 [S][K], pqs fp32 [K] or NULL, codes uint8 [S][K/2], scales uint8 [S][K/16], ts fp32 [1].
  * K % 16 == 0. Asynchronous on `stream`. */
+h3q_status h3q_debug_quantize_act(void* stream, const uint16_t* x, int64_t S, int64_t K, const float* pqs,
+                                  uint8_t* codes, uint8_t* scales, float* ts);
+/* The same entry point under its earlier name. */
 h3q_status h3q_quantize_nvfp4(void* stream, const uint16_t* x, int64_t S, int64_t K, const float* pqs,
                               uint8_t* codes, uint8_t* scales, float* ts);
 
-/* Diagnostic: the weight as the GEMM's decode stage sees it, E2M1 * E4M3 without the tensor scale
- * (exact in bf16), written to device bf16 [N][K]. Uses the same device decode as the GEMM. */
+/* Diagnostic (library convention): the weight as the GEMM's decode stage sees it, E2M1 * E4M3
+ * without the tensor scale (exact in bf16), written to device bf16 [N][K]. Uses the same device
+ * decode as the GEMM; it exists so that the decode can be compared with the format's definition
+ * bit for bit. */
 h3q_status h3q_debug_dequant(void* stream, h3q_weight w, uint16_t* wq);
 
-/* Diagnostic: 64-bit FNV-1a hash of the packed weight's device bytes (synchronizes `stream`).
- * Unchanged across any number of h3q_linear calls: the packed base is never written. */
+/* Diagnostic (library convention): 64-bit FNV-1a hash of the packed weight's device bytes
+ * (synchronizes `stream`). It makes the pages' rule checkable that the adapter is never merged into
+ * the packed base (FL2VA Turbo, "Implementation"): the hash is unchanged across any number of
+ * h3q_linear calls. */
 h3q_status h3q_weight_checksum(void* stream, h3q_weight w, uint64_t* out);
 
-/* Kernel timing with HIP events recorded on the call's stream around each launch of one kind.
+/* Measurement aid (library convention, not on the pages): kernel timing with HIP events recorded
+ * on the call's stream around each launch of one kind.
  * Off by default. h3q_timing_get waits for the recorded events, returns the summed milliseconds
  * and the number of launches of `kind` since the last get (or enable), and resets that kind. */
 enum { H3Q_KERNEL_GEMM = 0, H3Q_KERNEL_LORA_DOWN = 1, H3Q_KERNEL_PRESCALE = 2, H3Q_KERNEL_ACT_QUANT = 3 };
 h3q_status h3q_timing_enable(int32_t on);
 h3q_status h3q_timing_get(int32_t kind, double* total_ms, int64_t* launches);
 
-/* Thread-local description of the last failure on this thread ("" if none). */
+/* Thread-local description of the last failure on this thread ("" if none). Library convention. */
 const char* h3q_last_error(void);
 
 #ifdef __cplusplus

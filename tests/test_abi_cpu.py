@@ -28,11 +28,32 @@ def lib():
     return h3q.lib()
 
 
+# The boundary's entry points by the names the projection's C ABI gives them (the pack, register,
+# linear and SwiGLU calls, the flags entry point, the error text, and the test/diagnostic exports).
+SCOPE_NAMES = ("h3q_pack_weight", "h3q_free_weight", "h3q_register_adapter", "h3q_unregister_adapter",
+               "h3q_linear", "h3q_linear_swiglu", "h3q_linear_ex", "h3q_last_error", "h3q_debug_dequant",
+               "h3q_debug_quantize_act", "h3q_weight_checksum")
+PAGES = ("FL2VA Turbo", "MiniMax-H3 Ultra Fast", "MiniMax-H3 Turbo CMF card")
+
+
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("h3q_pack_weight", "h3q_register_adapter", "h3q_linear", "h3q_linear_swiglu",
-                     "h3q_linear_ex", "h3q_quantize_nvfp4", "h3q_last_error"):
-        assert required in names
+    missing = [n for n in SCOPE_NAMES if n not in names]
+    assert not missing, missing
+    assert "h3q_quantize_nvfp4" in names  # the quantizer's earlier name stays as an alias
+
+
+def test_every_entry_point_cites_a_page_or_says_it_is_a_convention():
+    """The comment block in front of each declaration (or of the group it belongs to) names the page
+    and section that defines the call, or says that the call is a library convention."""
+    text = open(HEADER).read()
+    for name in declared_functions():
+        m = re.search(r"(h3q_status|const char\*)\s+" + name + r"\s*\(", text)
+        before = text[:m.start()]
+        comment = before[before.rfind("/*"):]
+        assert "*/" in comment, name
+        ok = any(pg in comment for pg in PAGES) or "convention" in comment.lower() or "earlier name" in comment
+        assert ok, f"{name}: its comment cites no page and does not say it is a library convention"
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -115,9 +136,10 @@ def test_dead_handles_are_rejected(lib):
 def test_quantize_and_timing_argument_checks(lib):
     buf = np.zeros(64, np.uint8)
     p = ctypes.c_void_p(buf.ctypes.data)
-    assert lib.h3q_quantize_nvfp4(None, None, 1, 16, None, p, p, p) == h3q.H3Q_E_ARG
-    assert lib.h3q_quantize_nvfp4(None, p, 1, 24, None, p, p, p) == h3q.H3Q_E_SHAPE
-    assert lib.h3q_quantize_nvfp4(None, p, -1, 16, None, p, p, p) == h3q.H3Q_E_SHAPE
+    for fn in (lib.h3q_debug_quantize_act, lib.h3q_quantize_nvfp4):
+        assert fn(None, None, 1, 16, None, p, p, p) == h3q.H3Q_E_ARG
+        assert fn(None, p, 1, 24, None, p, p, p) == h3q.H3Q_E_SHAPE
+        assert fn(None, p, -1, 16, None, p, p, p) == h3q.H3Q_E_SHAPE
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.h3q_timing_get(7, ctypes.byref(ms), ctypes.byref(n)) == h3q.H3Q_E_ARG
     assert lib.h3q_timing_enable(0) == h3q.H3Q_OK

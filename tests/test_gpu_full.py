@@ -186,7 +186,54 @@ def test_rows_beyond_32bit_offsets(block):
     y_short = h3q.h3q_linear(x[:300].contiguous(), pqs, pr.handle, 1, 1.0)
     torch.cuda.synchronize()
     assert torch.equal(y[:300], y_short)
-    rows_per_launch = ((1 << 31) - 1) // (p.K * 2) // 128 * 128
-    edges = [np.arange(max(0, b - 96), min(S, b + 96)) for b in range(rows_per_launch, S, rows_per_launch)]
+    # the rows around each 1 GiB point of the activation (row 32768: 1 GiB, 65536: 2 GiB, the reach of
+    # a signed 32-bit offset from the buffer's start)
+    per_gib = (1 << 30) // (p.K * 2)
+    edges = [np.arange(max(0, b - 96), min(S, b + 96)) for b in range(per_gib, S, per_gib)]
     rows = np.unique(np.concatenate([np.arange(64), np.arange(0, S, 509), np.arange(S - 160, S)] + edges))
-    check_rows(pr, y, x, pqs, rows, 1, 1.0, "adapter 1, strength 1, across row ranges")
+    check_rows(pr, y, x, pqs, rows, 1, 1.0, "adapter 1, strength 1, around the 1 and 2 GiB points")
+
+
+SENTINEL = -12345.0  # exact in bf16
+
+
+def _guarded(rows, cols, post_rows=2):
+    """A [rows][cols] bf16 view with 64 sentinel elements before it and post_rows sentinel rows after it."""
+    buf = torch.full((64 + (rows + post_rows) * cols,), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    return buf, buf[64:64 + rows * cols].view(rows, cols), 64, rows * cols
+
+
+def _intact(buf, pre, n) -> bool:
+    return bool((buf[:pre] == SENTINEL).all() and (buf[pre + n:] == SENTINEL).all())
+
+
+@pytest.mark.parametrize("S", [wl.S_CANVAS, wl.S_CANVAS_ALT])
+def test_output_sentinels_full(block, S):
+    """Sentinel rows after the last row (the 94-row tail tile at S = 37726) and sentinels before the
+    first element stay untouched for the QKV projection (plain and with the fused Q/K epilogue) and the
+    gate/up SwiGLU projection with the emitted down operand; every output element is written."""
+    say(f"output sentinels S={S}")
+    i, p, pr = block["qkv"]
+    x, pqs = inputs(7, i, S, p.K)
+    buf, y, pre, n = _guarded(S, p.N)
+    h3q.h3q_linear(x, pqs, pr.handle, 1, 1.0, y=y)
+    torch.cuda.synchronize()
+    assert _intact(buf, pre, n) and not (y == SENTINEL).any(), "qkv plain"
+    q_width, rot = 6144, 96
+    g = synth.uniform((2, q_width), 0.5, 1.5, 7001, "cuda")
+    cos, sin = synth.rope_table(S, rot)
+    h3q.h3q_linear_qk_norm_rope(x, pqs, pr.handle, 1, 1.0, q_width, rot, 1e-6, g[0].contiguous(), g[1].contiguous(),
+                                cos.cuda(), sin.cuda(), y=y)
+    torch.cuda.synchronize()
+    assert _intact(buf, pre, n) and not (y == SENTINEL).any(), "qkv with the Q/K epilogue"
+    del buf, y, x
+    i, p, pr = block["gate_up"]
+    x, pqs = inputs(7, i, S, p.K)
+    F = p.N // 2
+    pqs_next = synth.pre_quant_scale(F, 7002, "cuda")
+    hb, h, hpre, hn = _guarded(S, F)
+    xb, xs, xpre, xn = _guarded(S, F)
+    h3q.h3q_linear_swiglu_emit(x, pqs, pr.handle, 1, 1.0, pqs_next, h=h, xs_next=xs)
+    torch.cuda.synchronize()
+    assert _intact(hb, hpre, hn) and _intact(xb, xpre, xn), "gate/up SwiGLU with emit"
+    assert not (h == SENTINEL).any() and not (xs == SENTINEL).any()

@@ -114,12 +114,13 @@ def test_mlp_chain_full_s8192():
         dn.free()
 
 
-def test_emit_across_row_ranges():
-    """K = 16384 puts more than 2 GiB of activation in S = 65836 rows, so the GEMM runs as two row
-    ranges (32-bit buffer offsets); the emitted operand of the second range must land in its own rows:
-    the fused chain stays bit-identical to the unfused one on every row."""
+def test_emit_past_2gib_of_activation():
+    """K = 16384 puts more than 2 GiB of activation in S = 65836 rows (one launch; the GEMM addresses
+    each tile from its own first row, so its 32-bit buffer offsets stay small). The emitted operand of
+    the rows past the 2 GiB point must land in their own rows: the fused chain stays bit-identical to
+    the unfused one on every row."""
     S, K, F, D = 65836, 16384, 256, 128
-    say(f"fusion chain across row ranges S={S} K={K}")
+    say(f"fusion chain past 2 GiB of activation S={S} K={K}")
     gu = Proj(2 * F, K, 1900, gate_up=True)
     dn = Proj(D, F, 1901)
     try:
@@ -130,7 +131,7 @@ def test_emit_across_row_ranges():
         pqs_dn = synth.pre_quant_scale(F, 1908, "cuda")
         h, y, h2, xs, y2 = chain(gu, dn, x, pqs_gu, pqs_dn, 1, 1.0)
         assert torch.equal(h, h2)
-        assert torch.equal(y, y2), "fused chain differs across the row ranges"
+        assert torch.equal(y, y2), "fused chain differs past 2 GiB of activation"
         say("  h and y bit-identical on all rows")
     finally:
         gu.free()

@@ -48,6 +48,7 @@ def _declare(lib):
         "h3q_linear": [vp, vp, i64, vp, vp, i32, f32, vp],
         "h3q_linear_swiglu": [vp, vp, i64, vp, vp, i32, f32, vp],
         "h3q_linear_ex": [vp, vp, i64, vp, vp, i32, f32, u32, vp],
+        "h3q_linear_ex_noalloc": [vp, vp, i64, vp, vp, i32, f32, u32, vp],
         "h3q_linear_qk_norm_rope": [vp, vp, i64, vp, vp, i32, f32, u32, i64, i32, f32, vp, vp, vp, vp, vp],
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_quantize_act": [vp, vp, i64, i64, vp, vp, vp, vp],
@@ -175,6 +176,16 @@ def h3q_weight_info(w: int):
 
 def h3q_linear_ex(x, pqs, w: int, adapter_id: int, strength: float, flags: int = 0, out=None, stream=None):
     """x: device bf16 [S][K]; pqs: device fp32 [K] or None. Returns out (allocated if None)."""
+    return _linear_ex(lib().h3q_linear_ex, x, pqs, w, adapter_id, strength, flags, out, stream)
+
+
+def h3q_linear_ex_noalloc(x, pqs, w: int, adapter_id: int, strength: float, flags: int = 0, out=None, stream=None):
+    """h3q_linear_ex with the workspace in the library's fixed device scratch (the library allocates
+    nothing; `out` is allocated here by torch if None)."""
+    return _linear_ex(lib().h3q_linear_ex_noalloc, x, pqs, w, adapter_id, strength, flags, out, stream)
+
+
+def _linear_ex(fn, x, pqs, w, adapter_id, strength, flags, out, stream):
     import torch
     N, K, _ = h3q_weight_info(w)
     S = x.shape[0]
@@ -187,9 +198,8 @@ def h3q_linear_ex(x, pqs, w: int, adapter_id: int, strength: float, flags: int =
         out = torch.empty((S, n_out), dtype=torch.bfloat16, device=x.device)
     elif tuple(out.shape) != (S, n_out):
         raise ValueError(f"out must be [{S}][{n_out}]")
-    _check(lib().h3q_linear_ex(_stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S,
-                               _dev_ptr(pqs, torch.float32, "pqs"), ctypes.c_void_p(w), int(adapter_id),
-                               float(strength), int(flags), _dev_ptr(out, torch.bfloat16, "out")))
+    _check(fn(_stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S, _dev_ptr(pqs, torch.float32, "pqs"),
+              ctypes.c_void_p(w), int(adapter_id), float(strength), int(flags), _dev_ptr(out, torch.bfloat16, "out")))
     return out
 
 

@@ -212,6 +212,30 @@ h3q_status workspace(int dev, hipStream_t stream, size_t need, uint8_t** out) {
   return H3Q_OK;
 }
 
+// ---- the fixed scratch of h3q_linear_ex_noalloc ----
+// A file-scope device array: every GPU the library runs on holds its own copy from the time the
+// library's code is loaded there until the process ends. In host code `scratch` is only a stand-in
+// for the symbol, never a device address: the address is looked up once per device, with that device
+// current, and only that pointer is handed to kernels.
+static_assert(H3Q_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[H3Q_NOALLOC_SCRATCH_BYTES];
+
+h3q_status scratch_on_device(int dev, uint8_t** out) {
+  static std::mutex mu;
+  static std::map<int, uint8_t*> ptrs;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(H3Q_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    it = ptrs.emplace(dev, static_cast<uint8_t*>(p)).first;
+  }
+  *out = it->second;
+  return H3Q_OK;
+}
+
 }  // namespace
 
 // ---- handles ----
@@ -442,7 +466,7 @@ struct FuseArgs {
 
 h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
                        int32_t adapter_id, float strength, uint32_t flags, uint16_t* out, const QkArgs* qk,
-                       const FuseArgs* fuse = nullptr) {
+                       const FuseArgs* fuse = nullptr, bool noalloc = false) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (!live(w)) return fail(H3Q_E_ARG, "linear: not a live weight handle");
   if (S != 0 && (!x || !out)) return fail(H3Q_E_ARG, "linear: null x or output");
@@ -490,7 +514,16 @@ h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float*
   const size_t act_bytes = direct_x ? 0 : static_cast<size_t>(round_up(S * w->K_pad * 2, 256));
   const size_t t_bytes = lora ? static_cast<size_t>(round_up(S * ad->r_pad * 2, 256)) : 0;
   uint8_t* ws = nullptr;
-  if (h3q_status st = workspace(dev, stream, small + act_bytes + t_bytes, &ws)) return st;
+  if (noalloc) {  // the fixed scratch: no allocation, no synchronization
+    const size_t need = small + act_bytes + t_bytes;
+    if (need > H3Q_NOALLOC_SCRATCH_BYTES)
+      return fail(H3Q_E_SHAPE, "linear_ex_noalloc: the call needs %zu bytes of scratch (S=%lld, K_pad=%lld, r_pad=%d); "
+                  "the fixed scratch holds %zu", need, (long long)S, (long long)w->K_pad, lora ? ad->r_pad : 0,
+                  static_cast<size_t>(H3Q_NOALLOC_SCRATCH_BYTES));
+    if (h3q_status st = scratch_on_device(dev, &ws)) return st;
+  } else if (h3q_status st = workspace(dev, stream, small + act_bytes + t_bytes, &ws)) {
+    return st;
+  }
   uint32_t* amax_bits = reinterpret_cast<uint32_t*>(ws);
   float* ts_a = reinterpret_cast<float*>(ws + 4);
   uint16_t* act = given_xs ? const_cast<uint16_t*>(fuse->xs)
@@ -558,6 +591,11 @@ h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float*
 h3q_status h3q_linear_ex(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
                          int32_t adapter_id, float strength, uint32_t flags, uint16_t* out) {
   return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags, out, nullptr);
+}
+
+h3q_status h3q_linear_ex_noalloc(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                                 int32_t adapter_id, float strength, uint32_t flags, uint16_t* out) {
+  return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags, out, nullptr, nullptr, true);
 }
 
 h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,

@@ -139,6 +139,20 @@ h3q_status h3q_linear_swiglu(void* stream, const uint16_t* x, int64_t S, const f
 h3q_status h3q_linear_ex(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
                          int32_t adapter_id, float strength, uint32_t flags, uint16_t* out);
 
+/* h3q_linear_ex for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels and the same results bit for
+ * bit, but the per-call workspace (the prescaled or quantized activation, t', the W4A4 scale) lives in
+ * a fixed device array of H3Q_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, so the call allocates nothing, frees nothing and never synchronizes.
+ * A call needs 256 + S * K_pad * 2 (unless pqs is NULL, K % 64 == 0 and the W4A4 flag is off) +
+ * S * r_pad * 2 (with an active adapter) bytes, K_pad = K rounded up to 64 and r_pad = rank rounded
+ * up to 32; a call that needs more fails with H3Q_E_SHAPE before anything is enqueued. Every call
+ * on one GPU shares that GPU's array, whatever its stream: calls that overlap in time on one GPU race
+ * on it, so the caller orders them (one stream, or events). Otherwise as h3q_linear_ex. */
+#define H3Q_NOALLOC_SCRATCH_BYTES (64u << 20)
+h3q_status h3q_linear_ex_noalloc(void* stream, const uint16_t* x, int64_t S, const float* pqs, h3q_weight w,
+                                 int32_t adapter_id, float strength, uint32_t flags, uint16_t* out);
+
 /* Producer fusion across the MLP (FL2VA Turbo, "Implementation": a producer that emits the next
  * projection's base input together with the exact bf16 LoRA input; on the pages' hardware it was
  * bit-exact and 3.08% slower, and the runtime kept the materialized path).
@@ -179,6 +193,7 @@ h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, c
                                    int32_t adapter_id, float strength, uint32_t flags, int64_t q_width,
                                    int32_t rot_dim, float eps, const float* gamma_q, const float* gamma_k,
                                    const float* rope_cos, const float* rope_sin, uint16_t* y);
+
 
 /* The merged route, for comparison with the dynamic path only: the adapter's update folded into the
  * weight before quantizing, as a converter that bakes a LoRA into a 4-bit checkpoint does (MiniMax-H3

@@ -50,6 +50,8 @@ def _declare(lib):
         "h3q_linear_ex": [vp, vp, i64, vp, vp, i32, f32, u32, vp],
         "h3q_linear_ex_noalloc": [vp, vp, i64, vp, vp, i32, f32, u32, vp],
         "h3q_linear_qk_norm_rope": [vp, vp, i64, vp, vp, i32, f32, u32, i64, i32, f32, vp, vp, vp, vp, vp],
+        "h3q_linear_qk_norm_rope_sections": [vp, vp, i64, vp, vp, i32, f32, u32, i64, i32, vp, i32, f32, vp, vp, vp,
+                                             vp, vp],
         "h3q_quantize_nvfp4": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_quantize_act": [vp, vp, i64, i64, vp, vp, vp, vp],
         "h3q_debug_dequant": [vp, vp, vp],
@@ -252,9 +254,11 @@ def h3q_linear_prescaled(x, xs, w: int, adapter_id: int, strength: float, y=None
 
 def h3q_linear_qk_norm_rope(x, pqs, w: int, adapter_id: int, strength: float, q_width: int, rot_dim: int,
                             eps: float, gamma_q, gamma_k, rope_cos=None, rope_sin=None, flags: int = 0, y=None,
-                            stream=None):
-    """Fused QKV projection + per-head Q/K RMSNorm + split-half rotation of the first rot_dim dims.
-    gamma_q, gamma_k: device fp32 [q_width]; rope_cos, rope_sin: device fp32 [S][rot_dim/2]."""
+                            stream=None, sections=None):
+    """Fused QKV projection + per-head Q/K RMSNorm + split-half rotation of the first rot_dim dims
+    (within each section of `sections`, consecutive widths summing to rot_dim, when given: the
+    h3q_linear_qk_norm_rope_sections entry point). gamma_q, gamma_k: device fp32 [q_width];
+    rope_cos, rope_sin: device fp32 [S][rot_dim/2]."""
     import torch
     N, K, _ = h3q_weight_info(w)
     S = x.shape[0]
@@ -273,12 +277,16 @@ def h3q_linear_qk_norm_rope(x, pqs, w: int, adapter_id: int, strength: float, q_
         y = torch.empty((S, N), dtype=torch.bfloat16, device=x.device)
     elif tuple(y.shape) != (S, N):
         raise ValueError(f"y must be [{S}][{N}]")
-    _check(lib().h3q_linear_qk_norm_rope(
-        _stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S, _dev_ptr(pqs, torch.float32, "pqs"), ctypes.c_void_p(w),
-        int(adapter_id), float(strength), int(flags), int(q_width), int(rot_dim), float(eps),
-        _dev_ptr(gamma_q, torch.float32, "gamma_q"), _dev_ptr(gamma_k, torch.float32, "gamma_k"),
-        _dev_ptr(rope_cos, torch.float32, "rope_cos"), _dev_ptr(rope_sin, torch.float32, "rope_sin"),
-        _dev_ptr(y, torch.bfloat16, "y")))
+    common = (_dev_ptr(gamma_q, torch.float32, "gamma_q"), _dev_ptr(gamma_k, torch.float32, "gamma_k"),
+              _dev_ptr(rope_cos, torch.float32, "rope_cos"), _dev_ptr(rope_sin, torch.float32, "rope_sin"),
+              _dev_ptr(y, torch.bfloat16, "y"))
+    head = (_stream(stream), _dev_ptr(x, torch.bfloat16, "x"), S, _dev_ptr(pqs, torch.float32, "pqs"),
+            ctypes.c_void_p(w), int(adapter_id), float(strength), int(flags), int(q_width), int(rot_dim))
+    if sections is None:
+        _check(lib().h3q_linear_qk_norm_rope(*head, float(eps), *common))
+    else:
+        sec = (ctypes.c_int32 * max(len(sections), 1))(*[int(v) for v in sections])
+        _check(lib().h3q_linear_qk_norm_rope_sections(*head, sec, len(sections), float(eps), *common))
     return y
 
 
@@ -394,3 +402,12 @@ def h3q_timing_get(kind: int):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(lib().h3q_timing_get(int(kind), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def h3q_linear_qk_norm_rope_sections(x, pqs, w: int, adapter_id: int, strength: float, q_width: int, rot_dim: int,
+                                     sections, eps: float, gamma_q, gamma_k, rope_cos=None, rope_sin=None,
+                                     flags: int = 0, y=None, stream=None):
+    """h3q_linear_qk_norm_rope with the rotated dims in axis sections, each rotated in split halves
+    within itself (`sections`: consecutive even widths summing to rot_dim)."""
+    return h3q_linear_qk_norm_rope(x, pqs, w, adapter_id, strength, q_width, rot_dim, eps, gamma_q, gamma_k,
+                                   rope_cos, rope_sin, flags, y, stream, sections=list(sections))

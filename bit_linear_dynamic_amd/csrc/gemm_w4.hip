@@ -433,18 +433,22 @@ __device__ __forceinline__ void swiglu_epilogue_staged(const GemmParams& p, cons
 }
 
 // Q/K tiles of the fused QKV projection (MiniMax-H3 Ultra Fast, "Active optimization stack",
-// attention projections, and "Kernel path" item 2; 96 of 128 head dimensions rotate: MiniMax-H3
-// Turbo CMF card, "On parity"). The tile's 256 columns are two heads of 128. Per row and head:
+// attention projections, and "Kernel path" item 2: three-axis split-half rotary; 96 of 128 head
+// dimensions rotate: MiniMax-H3 Turbo CMF card, "On parity"). The tile's 256 columns are two heads of
+// 128. Per row and head:
 //   u_i = v_i / sqrt(mean_j v_j^2 + eps) * gamma_i            (v = ts * acc, fp32)
-//   out_i = u_i c_i - u_{i+h} s_i,  out_{i+h} = u_{i+h} c_i + u_i s_i   (i < h = rot/2)
+// then the first rot dims, as consecutive sections of widths w_j, each rotated in split halves
+// within itself (section at dims [o, o + w), h = w / 2, table column o/2 + i for its pair i):
+//   out_{o+i} = u_{o+i} c - u_{o+i+h} s,  out_{o+i+h} = u_{o+i+h} c + u_{o+i} s
 //   out_i = u_i                                               (rot <= i < 128)
-// with c, s the caller's per-row angle table. The fp32 tile goes through the freed LDS 128 rows at
-// a time ([128][260] floats: 16-byte aligned rows, and 16-byte reads of 8 consecutive rows fall on
-// distinct banks), with the tile's 256 gamma values beside it; then one thread per (row, head) sums
-// the head's squares with 16-byte reads, and normalizes and rotates 8 pairs at a time in place (one
-// pair at a time when h is not a multiple of 8); then the tile is stored as bf16 by 32 threads per
-// row, whole row segments per store instruction. The row's angle table is loaded into registers
-// before the pass's staging, so its latency hides behind the LDS writes and the barrier.
+// with c, s the caller's per-row angle table (one section of rot: pair i is dims i and i + rot/2).
+// The fp32 tile goes through the freed LDS 128 rows at a time ([128][260] floats: 16-byte aligned
+// rows, and 16-byte reads of 8 consecutive rows fall on distinct banks), with the tile's 256 gamma
+// values beside it; then one thread per (row, head) sums the head's squares with 16-byte reads, and
+// normalizes and rotates 8 pairs at a time in place (one pair at a time when a section's half is not
+// a multiple of 8); then the tile is stored as bf16 by 32 threads per row, whole row segments per
+// store instruction. The row's angle table is loaded into registers before the pass's staging, so
+// its latency hides behind the LDS writes and the barrier.
 constexpr int kQkPitch = 260;
 constexpr int kQkRows = 128;
 constexpr uint32_t kQkGamma = kQkRows * kQkPitch * 4;
@@ -474,10 +478,10 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
   const int tid = threadIdx.x;
   const float* gamma_tile = is_q ? p.qk_gamma_q + static_cast<int64_t>(nt) * BN
                                  : p.qk_gamma_k + static_cast<int64_t>(nt - p.q_tiles) * BN;
-  const int half = p.rope_half;
+  const int half = p.rope_half;  // angle table columns per row (rot / 2)
   const int head = __builtin_amdgcn_readfirstlane(tid >> 7);  // waves 0, 1: head 0; waves 2, 3: head 1
   const int row_l = tid & (kQkRows - 1);
-  const bool vec = (half & 7) == 0;
+  const bool vec = p.rope_vec != 0;
   const bool vec_tab = vec && ((reinterpret_cast<uintptr_t>(p.rope_cos) | reinterpret_cast<uintptr_t>(p.rope_sin)) & 15) == 0;
 #pragma unroll
   for (int pass = 0; pass < BM / kQkRows; ++pass) {
@@ -524,13 +528,14 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
       if (vec) {
 #pragma unroll
         for (int gi = 0; gi < 8; ++gi) {
-          const int i = gi * 8;
+          const int i = gi * 8;  // table columns i .. i + 7
           if (i >= half) break;
+          const int dlo = p.rope_lo[gi], dhi = p.rope_hi[gi];
           float tv[8], th[8], gv[8], gh[8], cs[8], sn[8], lo[8], hi[8];
-          load8(t + i, tv);
-          load8(t + i + half, th);
-          load8(g + i, gv);
-          load8(g + i + half, gh);
+          load8(t + dlo, tv);
+          load8(t + dhi, th);
+          load8(g + dlo, gv);
+          load8(g + dhi, gh);
           if (vec_tab) {
             const f32x4 c0 = cpre[2 * gi], c1 = cpre[2 * gi + 1], s0 = spre[2 * gi], s1 = spre[2 * gi + 1];
             cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w; cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
@@ -548,8 +553,8 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
             lo[e] = a * cs[e] - b * sn[e];
             hi[e] = b * cs[e] + a * sn[e];
           }
-          store8(t + i, lo);
-          store8(t + i + half, hi);
+          store8(t + dlo, lo);
+          store8(t + dhi, hi);
         }
         for (int k = 2 * half; k < 128; k += 8) {
           float tv[8], gv[8], u[8];
@@ -559,12 +564,18 @@ __device__ __forceinline__ void qk_norm_rope_epilogue(const GemmParams& p, const
           for (int e = 0; e < 8; ++e) u[e] = tv[e] * inv * gv[e];
           store8(t + k, u);
         }
-      } else {  // h not a multiple of 8: one pair at a time
-        for (int i = 0; i < half; ++i) {
-          const float a = t[i] * inv * g[i], b = t[i + half] * inv * g[i + half];
-          const float c = cr[i], sv = sr[i];
-          t[i] = a * c - b * sv;
-          t[i + half] = b * c + a * sv;
+      } else {  // a section's half is not a multiple of 8: one pair at a time
+        int o = 0;
+        for (int j = 0; j < p.rope_nsec; ++j) {
+          const int h = p.rope_sec[j] / 2;
+          for (int i = 0; i < h; ++i) {
+            const int lo = o + i, hi = o + i + h;
+            const float a = t[lo] * inv * g[lo], b = t[hi] * inv * g[hi];
+            const float c = cr[o / 2 + i], sv = sr[o / 2 + i];
+            t[lo] = a * c - b * sv;
+            t[hi] = b * c + a * sv;
+          }
+          o += p.rope_sec[j];
         }
         for (int k = 2 * half; k < 128; ++k) t[k] = t[k] * inv * g[k];
       }

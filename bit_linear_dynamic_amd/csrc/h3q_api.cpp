@@ -454,6 +454,8 @@ struct QkArgs {
   int32_t rot_dim;
   float eps;
   const float *gamma_q, *gamma_k, *cos, *sin;
+  int32_t nsec;      // sections of the rotated dims (validated: 1..4, even, summing to rot_dim)
+  int32_t sec[4];
 };
 
 // Producer fusion: the SwiGLU epilogue also writes the next projection's base operand
@@ -579,6 +581,18 @@ h3q_status linear_impl(void* stream_, const uint16_t* x, int64_t S, const float*
     g.q_tiles = static_cast<int32_t>(qk->q_width / kGemmBN);
     g.rope_half = qk->rot_dim / 2;
     g.qk_eps = qk->eps;
+    g.rope_nsec = qk->nsec;
+    g.rope_vec = 1;
+    for (int j = 0, o = 0, col = 0; j < qk->nsec; ++j) {
+      g.rope_sec[j] = qk->sec[j];
+      const int h = qk->sec[j] / 2;
+      if (h % 8 != 0) g.rope_vec = 0;
+      for (int i = 0; i + 8 <= h && col < 64; i += 8, col += 8) {  // pair groups of 8 table columns
+        g.rope_lo[col / 8] = o + i;
+        g.rope_hi[col / 8] = o + i + h;
+      }
+      o += qk->sec[j];
+    }
     epi = Epilogue::QkNormRope;
   }
   e = timed(H3Q_KERNEL_GEMM, stream, [&] { return launch_gemm_w4(g, epi, stream); });
@@ -602,6 +616,17 @@ h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, c
                                    int32_t adapter_id, float strength, uint32_t flags, int64_t q_width,
                                    int32_t rot_dim, float eps, const float* gamma_q, const float* gamma_k,
                                    const float* rope_cos, const float* rope_sin, uint16_t* y) {
+  return h3q_linear_qk_norm_rope_sections(stream, x, S, pqs, w, adapter_id, strength, flags, q_width, rot_dim,
+                                          &rot_dim, rot_dim > 0 ? 1 : 0, eps, gamma_q, gamma_k, rope_cos, rope_sin,
+                                          y);
+}
+
+h3q_status h3q_linear_qk_norm_rope_sections(void* stream, const uint16_t* x, int64_t S, const float* pqs,
+                                            h3q_weight w, int32_t adapter_id, float strength, uint32_t flags,
+                                            int64_t q_width, int32_t rot_dim, const int32_t* sections,
+                                            int32_t n_sections, float eps, const float* gamma_q,
+                                            const float* gamma_k, const float* rope_cos, const float* rope_sin,
+                                            uint16_t* y) {
   if (!live(w)) return fail(H3Q_E_ARG, "qk_norm_rope: not a live weight handle");
   if ((flags & ~static_cast<uint32_t>(H3Q_ACT_NVFP4)) != 0)
     return fail(H3Q_E_ARG, "qk_norm_rope: only H3Q_ACT_NVFP4 may be set (got flags 0x%x)", flags);
@@ -615,7 +640,20 @@ h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, c
   if (!gamma_q || !gamma_k || (rot_dim > 0 && (!rope_cos || !rope_sin)))
     return fail(H3Q_E_ARG, "qk_norm_rope: null gamma or angle table");
   if (S != 0 && !aligned16(y)) return fail(H3Q_E_ARG, "qk_norm_rope: y must be 16-byte aligned");
-  const QkArgs qk{q_width, rot_dim, eps, gamma_q, gamma_k, rope_cos, rope_sin};
+  QkArgs qk{q_width, rot_dim, eps, gamma_q, gamma_k, rope_cos, rope_sin, 0, {0, 0, 0, 0}};
+  if (rot_dim > 0) {
+    if (!sections || n_sections < 1 || n_sections > 4)
+      return fail(H3Q_E_SHAPE, "qk_norm_rope: need 1 to 4 rotary sections (got %d)", n_sections);
+    int32_t sum = 0;
+    for (int32_t j = 0; j < n_sections; ++j) {
+      if (sections[j] <= 0 || sections[j] % 2 != 0)
+        return fail(H3Q_E_SHAPE, "qk_norm_rope: rotary section %d has width %d (must be even and > 0)", j, sections[j]);
+      sum += sections[j];
+      qk.sec[j] = sections[j];
+    }
+    if (sum != rot_dim) return fail(H3Q_E_SHAPE, "qk_norm_rope: rotary sections sum to %d, rot_dim is %d", sum, rot_dim);
+    qk.nsec = n_sections;
+  }
   return linear_impl(stream, x, S, pqs, w, adapter_id, strength, flags, y, &qk);
 }
 

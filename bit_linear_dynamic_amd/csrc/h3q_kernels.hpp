@@ -46,8 +46,16 @@ struct GemmParams {
   const float* rope_cos;    // fp32 [S][rope_half]
   const float* rope_sin;    // fp32 [S][rope_half]
   int32_t q_tiles;
-  int32_t rope_half;        // rotated pairs per 128-wide head (rot_dim / 2)
+  int32_t rope_half;        // rotated pairs per 128-wide head (rot_dim / 2): the angle table's columns
   float qk_eps;
+  // the rotated dims as consecutive sections, each rotated in split halves within itself; table
+  // columns follow the sections in order (one section of rot_dim: pair i is dims i and i + rot_dim/2)
+  int32_t rope_nsec;        // 1..4
+  int32_t rope_sec[4];      // section widths (even, summing to rot_dim)
+  // when every section's half is a multiple of 8 (rope_vec), pair group g (table columns 8g..8g+7)
+  // rotates dims rope_lo[g] + e with rope_hi[g] + e, e < 8
+  int32_t rope_vec;
+  int32_t rope_lo[8], rope_hi[8];
   // SwiGLU epilogue only, optional: also write the next projection's base operand
   // emit_out[s][n] = bf16(f32(h[s][n]) * emit_pqs[n]) (16-byte aligned rows, n_out % 8 == 0)
   const float* emit_pqs;    // fp32 [n_out]

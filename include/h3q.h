@@ -194,6 +194,23 @@ h3q_status h3q_linear_qk_norm_rope(void* stream, const uint16_t* x, int64_t S, c
                                    int32_t rot_dim, float eps, const float* gamma_q, const float* gamma_k,
                                    const float* rope_cos, const float* rope_sin, uint16_t* y);
 
+/* The same with the rotated dims split into axis sections (MiniMax-H3 Ultra Fast, "Kernel path",
+ * item 2: a three-axis split-half rotary). The pages do not say whether the split halves pair over
+ * all rotated dims or within each axis's dims; this call serves either reading. The first rot_dim
+ * dims of a head are n_sections consecutive sections of widths sections[0..n_sections) (host
+ * int32, each even and > 0, summing to rot_dim, 1 <= n_sections <= 4; ignored when rot_dim is 0), and
+ * each section is rotated in split halves within itself: for the section at dims [o, o + w) with
+ * h = w / 2 and its table columns [o/2, o/2 + h),
+ *   y_{o+i} = u_{o+i} * c - u_{o+i+h} * s,  y_{o+i+h} = u_{o+i+h} * c + u_{o+i} * s,
+ *   c = rope_cos[row][o/2 + i], s = rope_sin[row][o/2 + i]      (i < h)
+ * One section of rot_dim is h3q_linear_qk_norm_rope; three sections of 32 pair each axis's dims
+ * within the axis. Bad sections -> H3Q_E_SHAPE. Otherwise as h3q_linear_qk_norm_rope. */
+h3q_status h3q_linear_qk_norm_rope_sections(void* stream, const uint16_t* x, int64_t S, const float* pqs,
+                                            h3q_weight w, int32_t adapter_id, float strength, uint32_t flags,
+                                            int64_t q_width, int32_t rot_dim, const int32_t* sections,
+                                            int32_t n_sections, float eps, const float* gamma_q,
+                                            const float* gamma_k, const float* rope_cos, const float* rope_sin,
+                                            uint16_t* y);
 
 /* The merged route, for comparison with the dynamic path only: the adapter's update folded into the
  * weight before quantizing, as a converter that bakes a LoRA into a 4-bit checkpoint does (MiniMax-H3

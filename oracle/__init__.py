@@ -64,7 +64,7 @@ def _declare(lib):
     lib.orc_linear.argtypes = [vp, i64, i64, vp, vp, vp, f32, i64, vp, vp, i64, f64, f64, vp, vp, f32, vp]
     lib.orc_linear.restype = i32
     lib.orc_swiglu.argtypes, lib.orc_swiglu.restype = [vp, i64, i64, vp], None
-    lib.orc_qk_norm_rope.argtypes = [vp, i64, i64, i64, i32, f64, vp, vp, vp, vp, vp]
+    lib.orc_qk_norm_rope.argtypes = [vp, i64, i64, i64, i32, f64, vp, vp, vp, vp, vp, i32, vp]
     lib.orc_qk_norm_rope.restype = None
     lib.orc_merge_lora.argtypes = [vp, vp, f32, i64, i64, vp, vp, i64, f64, f64, vp, vp]
     lib.orc_merge_lora.restype = i32
@@ -183,20 +183,29 @@ def swiglu(y: np.ndarray, lib=None) -> np.ndarray:
 
 
 def qk_norm_rope(y: np.ndarray, q_width: int, rot_dim: int, eps: float, gamma_q, gamma_k, cos, sin,
-                 lib=None) -> np.ndarray:
-    """fp64 [M][N] fused-QKV output -> per-head RMSNorm of q and k, then split-half rotation of
-    their first rot_dim dims with the [M][rot_dim/2] angle tables; v unchanged (see oracle.cpp)."""
+                 sections=None, lib=None) -> np.ndarray:
+    """fp64 [M][N] fused-QKV output -> per-head RMSNorm of q and k, then rotation of their first
+    rot_dim dims with the [M][rot_dim/2] angle tables, in split halves within each section of
+    `sections` (consecutive widths summing to rot_dim; None: one section of rot_dim); v unchanged
+    (see oracle.cpp)."""
     y = _c(y, np.float64)
     M, N = y.shape
     if q_width % 128 or 2 * q_width > N or rot_dim % 2 or not 0 <= rot_dim <= 128:
         raise ValueError("qk_norm_rope: bad q_width or rot_dim")
+    sec = None
+    if sections is not None:
+        sec = _c(np.asarray(sections, np.int32), np.int32)
+        if sec.sum() != rot_dim or np.any(sec <= 0) or np.any(sec % 2):
+            raise ValueError("qk_norm_rope: sections must be positive, even and sum to rot_dim")
     half = rot_dim // 2
     cos = _c(np.asarray(cos, np.float32).reshape(M, half), np.float32)
     sin = _c(np.asarray(sin, np.float32).reshape(M, half), np.float32)
     out = np.empty_like(y)
     gamma_q, gamma_k = _c(gamma_q, np.float32), _c(gamma_k, np.float32)
     (lib or load()).orc_qk_norm_rope(_ptr(y), M, N, int(q_width), int(rot_dim), float(eps),
-                                     _ptr(gamma_q), _ptr(gamma_k), _ptr(cos), _ptr(sin), _ptr(out))
+                                     _ptr(gamma_q), _ptr(gamma_k), _ptr(cos), _ptr(sin),
+                                     None if sec is None else _ptr(sec), 0 if sec is None else len(sec),
+                                     _ptr(out))
     return out
 
 

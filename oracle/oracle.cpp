@@ -236,23 +236,33 @@ void orc_swiglu(const double* y, int64_t M, int64_t F, double* h) {
 }
 
 // Q/K RMSNorm and partial split-half rotary embedding on a fused QKV output (MiniMax-H3 Ultra
-// Fast, "Active optimization stack" (attention projections) and "Kernel path" item 2; which 96 of
-// the 128 head dimensions rotate: MiniMax-H3 Turbo CMF card, "On parity"). y holds M rows of
-// [q (qw) | k (qw) | v (rest)]; q and k are split into heads of 128 consecutive columns. Per row and
-// head, in this order:
+// Fast, "Active optimization stack" (attention projections) and "Kernel path" item 2: a three-axis
+// split-half rotary; which 96 of the 128 head dimensions rotate: MiniMax-H3 Turbo CMF card, "On
+// parity"). y holds M rows of [q (qw) | k (qw) | v (rest)]; q and k are split into heads of 128
+// consecutive columns. Per row and head, in this order:
 //   1. RMSNorm over the head:  u_i = y_i / sqrt( (1/128) sum_j y_j^2 + eps ) * gamma[head*128 + i]
 //      (gamma_q for q heads, gamma_k for k heads);
-//   2. rotate the first rot dims in split halves: with h = rot/2 and angle table entries
-//      c = cos[m][i], s = sin[m][i] for i < h:
-//        out_i     = u_i * c - u_{i+h} * s
-//        out_{i+h} = u_{i+h} * c + u_i * s
+//   2. rotate the first rot dims. They form n_sec consecutive sections of widths sec[0], sec[1], ...
+//      (summing to rot; one section of rot when sec is NULL), and each section is rotated in split
+//      halves within itself: for section j at dims [o, o + w) with h = w / 2, the angle table
+//      columns [o/2, o/2 + h) belong to it, and with c = cos[m][o/2 + i], s = sin[m][o/2 + i]:
+//        out_{o+i}   = u_{o+i} * c - u_{o+i+h} * s
+//        out_{o+i+h} = u_{o+i+h} * c + u_{o+i} * s          (i < h)
 //      and out_i = u_i for rot <= i < 128.
-// v columns are copied unchanged. cos/sin are [M][rot/2] (the caller's per-token angle table).
+// The two readings of "three-axis split-half" are one section of 96 (the halves pair dim i with
+// i + 48, the axes living only in the table's columns) and three sections of 32 (each axis's dims
+// pair within the axis). v columns are copied unchanged. cos/sin are [M][rot/2] (the caller's
+// per-token angle table).
 void orc_qk_norm_rope(const double* y, int64_t M, int64_t N, int64_t qw, int32_t rot, double eps,
                       const float* gamma_q, const float* gamma_k, const float* cos_t, const float* sin_t,
-                      double* out) {
+                      const int32_t* sec, int32_t n_sec, double* out) {
   const int64_t hd = 128;
-  const int64_t half = rot / 2;
+  const int64_t tab = rot / 2;
+  const int32_t one[1] = {rot};
+  if (!sec) {
+    sec = one;
+    n_sec = 1;
+  }
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static)
 #endif
@@ -268,10 +278,15 @@ void orc_qk_norm_rope(const double* y, int64_t M, int64_t N, int64_t qw, int32_t
       double u[128];
       for (int64_t i = 0; i < hd; ++i) u[i] = yr[c0 + i] * inv * static_cast<double>(gamma[i]);
       for (int64_t i = 0; i < hd; ++i) orow[c0 + i] = u[i];
-      for (int64_t i = 0; i < half; ++i) {
-        const double c = cos_t[m * half + i], s = sin_t[m * half + i];
-        orow[c0 + i] = u[i] * c - u[i + half] * s;
-        orow[c0 + i + half] = u[i + half] * c + u[i] * s;
+      int64_t o = 0;
+      for (int32_t j = 0; j < n_sec; ++j) {
+        const int64_t half = sec[j] / 2;
+        for (int64_t i = 0; i < half; ++i) {
+          const double c = cos_t[m * tab + o / 2 + i], s = sin_t[m * tab + o / 2 + i];
+          orow[c0 + o + i] = u[o + i] * c - u[o + i + half] * s;
+          orow[c0 + o + i + half] = u[o + i + half] * c + u[o + i] * s;
+        }
+        o += sec[j];
       }
     }
   }

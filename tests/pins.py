@@ -461,6 +461,39 @@ def pin_rope_complex_rotation(lib):
         assert np.array_equal(got[:, 2 * qw:], y[:, 2 * qw:])
 
 
+def pin_rope_sections_complex_rotation(lib):
+    """Rotation within axis sections: with sections of widths w_j at dims [o_j, o_j + w_j), dims
+    (o_j + i, o_j + i + w_j/2) of a normalized head form u + j v, multiplied by exp(j theta) with
+    theta from table column o_j/2 + i (numpy complex arithmetic); three sections of 32 is the per-axis
+    reading of the three-axis rotary, one section of rot_dim must equal the call without sections bit
+    for bit, and sections of unequal widths are checked too."""
+    rng = np.random.default_rng(37)
+    M = 4
+    y, qw, gq, gk = _qkv_case(rng, M, 2)
+    for sections in ((32, 32, 32), (16, 48, 32), (8, 4, 20), (96,), (128,)):
+        rot = sum(sections)
+        half = rot // 2
+        theta = rng.uniform(-np.pi, np.pi, (M, half))
+        cos, sin = np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+        flat = oracle.qk_norm_rope(y, qw, rot, 1e-6, gq, gk, np.ones((M, half)), np.zeros((M, half)), lib=lib)
+        got = oracle.qk_norm_rope(y, qw, rot, 1e-6, gq, gk, cos, sin, sections=sections, lib=lib)
+        rot_c = cos.astype(np.float64) + 1j * sin.astype(np.float64)
+        for c0 in range(0, 2 * qw, 128):
+            u = flat[:, c0:c0 + 128]
+            o = 0
+            for w in sections:
+                h = w // 2
+                z = (u[:, o:o + h] + 1j * u[:, o + h:o + w]) * rot_c[:, o // 2:o // 2 + h]
+                np.testing.assert_allclose(got[:, c0 + o:c0 + o + h], z.real, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(got[:, c0 + o + h:c0 + o + w], z.imag, rtol=1e-12, atol=1e-12)
+                o += w
+            assert np.array_equal(got[:, c0 + rot:c0 + 128], u[:, rot:])
+        assert np.array_equal(got[:, 2 * qw:], y[:, 2 * qw:])
+        if len(sections) == 1:
+            plain = oracle.qk_norm_rope(y, qw, rot, 1e-6, gq, gk, cos, sin, lib=lib)
+            assert np.array_equal(plain, got)
+
+
 def pin_merge_reproduces_dynamic_linear(lib):
     """The merged fp32 weight applied to x (*) pqs reproduces the dynamic linear (itself pinned to
     numpy and exact fractions) up to m's one fp32 rounding, for pqs != 1, alpha != rank, negative

@@ -41,7 +41,8 @@ def off_by_one_float(t):
     return v
 
 
-def run_case(p: Proj, x, pqs, q_width, rot, adapter_id, strength, flags=0, rows=None, misaligned_tables=False):
+def run_case(p: Proj, x, pqs, q_width, rot, adapter_id, strength, flags=0, rows=None, misaligned_tables=False,
+             sections=None):
     S = x.shape[0]
     gq, gk = gammas(q_width, 900 + q_width + rot)
     cos, sin = synth.rope_table(S, rot)
@@ -50,7 +51,8 @@ def run_case(p: Proj, x, pqs, q_width, rot, adapter_id, strength, flags=0, rows=
     if rot and misaligned_tables:
         cos_d, sin_d = off_by_one_float(cos), off_by_one_float(sin)
     y = h3q.h3q_linear_qk_norm_rope(x.to(dev), pqs.to(dev) if pqs is not None else None, p.handle, adapter_id,
-                                    strength, q_width, rot, EPS, gq.to(dev), gk.to(dev), cos_d, sin_d, flags=flags)
+                                    strength, q_width, rot, EPS, gq.to(dev), gk.to(dev), cos_d, sin_d, flags=flags,
+                                    sections=sections)
     plain = h3q.h3q_linear_ex(x.to(dev), pqs.to(dev) if pqs is not None else None, p.handle, adapter_id, strength,
                               flags)
     torch.cuda.synchronize()
@@ -61,7 +63,8 @@ def run_case(p: Proj, x, pqs, q_width, rot, adapter_id, strength, flags=0, rows=
     lin = p.reference(xb, pq, adapter_id, strength, w4a4=bool(flags & h3q.H3Q_ACT_NVFP4)) if rows is None else None
     if rows is not None:  # W4A4 is not run on row samples (its activation scale spans all rows)
         lin = p.reference(xb, pq, adapter_id, strength)
-    ref = oracle.qk_norm_rope(lin, q_width, rot, EPS, gq.numpy(), gk.numpy(), cos.numpy()[sel], sin.numpy()[sel])
+    ref = oracle.qk_norm_rope(lin, q_width, rot, EPS, gq.numpy(), gk.numpy(), cos.numpy()[sel], sin.numpy()[sel],
+                              sections=sections)
     ys = y.index_select(0, torch.from_numpy(sel).cuda())
     eq = normwise(ys[:, :q_width], ref[:, :q_width])
     ek = normwise(ys[:, q_width:2 * q_width], ref[:, q_width:2 * q_width])
@@ -94,6 +97,56 @@ def test_qk_norm_rope_parity(S, K, q_width, extra, rot, rank):
         pqs = synth.pre_quant_scale(K, 1104)
         for aid, st in ((NONE, 0.0), (1, 1.0)):
             run_case(p, x, pqs, q_width, rot, aid, st)
+    finally:
+        p.free()
+
+
+SECTION_CASES = [
+    # S, K, q_width, rank, sections: three axes of 32 dims each (the per-axis reading of the
+    # three-axis split-half rotary), unequal axes, halves that are not multiples of 8 (one pair at a
+    # time), two sections over all 128 dims
+    (300, 512, 256, 64, (32, 32, 32)),
+    (77, 208, 512, 16, (16, 48, 32)),
+    (129, 256, 256, 64, (24, 40, 32)),
+    (64, 320, 256, 384, (64, 64)),
+]
+
+
+@pytest.mark.parametrize("S,K,q_width,rank,sections", SECTION_CASES)
+def test_qk_norm_rope_sections_parity(S, K, q_width, rank, sections):
+    """Rotation within axis sections (h3q_linear_qk_norm_rope_sections) against the oracle."""
+    rot = sum(sections)
+    say(f"qk sections {sections} S={S} K={K} q_width={q_width} r={rank}")
+    p = Proj(3 * q_width, K, 1400 + S + K)
+    try:
+        p.add_adapter(1, rank, float(rank), 1401, 1402)
+        x, pqs = synth.activation(S, K, 1403), synth.pre_quant_scale(K, 1404)
+        for aid, st in ((NONE, 0.0), (1, 1.0)):
+            run_case(p, x, pqs, q_width, rot, aid, st, sections=sections)
+        run_case(p, x, pqs, q_width, rot, 1, 1.0, flags=h3q.H3Q_ACT_NVFP4, sections=sections)
+        run_case(p, x, pqs, q_width, rot, 1, 1.0, misaligned_tables=True, sections=sections)
+    finally:
+        p.free()
+
+
+def test_qk_norm_rope_one_section_is_the_plain_call():
+    """One section of rot_dim is the reading of h3q_linear_qk_norm_rope, bit for bit; three sections
+    of 32 give a different result (the two readings differ)."""
+    S, K, q_width = 200, 256, 256
+    p = Proj(3 * q_width, K, 1500)
+    try:
+        p.add_adapter(1, 64, 64.0, 1501, 1502)
+        x, pqs = synth.activation(S, K, 1503).cuda(), synth.pre_quant_scale(K, 1504).cuda()
+        gq, gk = (g.cuda() for g in gammas(q_width, 1505))
+        cos, sin = (t.cuda() for t in synth.rope_table(S, 96))
+        args = (x, pqs, p.handle, 1, 1.0, q_width, 96, EPS, gq, gk, cos, sin)
+        plain = h3q.h3q_linear_qk_norm_rope(*args)
+        one = h3q.h3q_linear_qk_norm_rope(*args, sections=(96,))
+        three = h3q.h3q_linear_qk_norm_rope(*args, sections=(32, 32, 32))
+        torch.cuda.synchronize()
+        assert torch.equal(plain, one)
+        assert not torch.equal(plain[:, :2 * q_width], three[:, :2 * q_width])
+        assert torch.equal(plain[:, 2 * q_width:], three[:, 2 * q_width:])
     finally:
         p.free()
 
@@ -136,6 +189,8 @@ def test_qk_norm_rope_full_qkv_s8192():
         pqs = synth.pre_quant_scale(P.K, synth.seed_of(7, 0, synth.PQS))
         rows = np.unique(np.concatenate([np.arange(256), np.arange(256, S - 256, 128), np.arange(S - 256, S)]))
         run_case(p, x, pqs, wl.D_MODEL, 96, 1, 1.0, rows=rows)
+        say("  per-axis sections (32, 32, 32)")
+        run_case(p, x, pqs, wl.D_MODEL, 96, 1, 1.0, rows=rows, sections=(32, 32, 32))
     finally:
         p.free()
 
@@ -166,6 +221,8 @@ def test_qk_norm_rope_argument_errors():
         expect(h3q.H3Q_E_ARG, flags=h3q.H3Q_EPI_SWIGLU)
         expect(h3q.H3Q_E_ARG, handle=gu.handle, q_width=256)
         expect(h3q.H3Q_E_ARG, flags=1 << 7)
+        for bad in ((32, 32), (32, 33, 31), (0, 64, 32), (16, 16, 16, 16, 32), (-32, 64, 64)):
+            expect(h3q.H3Q_E_SHAPE, sections=bad)
     finally:
         p.free()
         gu.free()

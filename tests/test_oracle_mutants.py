@@ -46,11 +46,18 @@ MUTANTS = [
     ("silu_sign", "g / (1.0 + std::exp(-g)) * u", "g / (1.0 + std::exp(g)) * u", 0),
     ("gate_up_swapped", "g = y[m * 2 * F + j], u = y[m * 2 * F + F + j]", "u = y[m * 2 * F + j], g = y[m * 2 * F + F + j]", 0),
     ("prescale_f32_no_pqs", "const double p = pqs ? static_cast<double>(pqs[k]) : 1.0;", "const double p = 1.0;", 0),
-    ("rope_sign", "orow[c0 + i] = u[i] * c - u[i + half] * s;", "orow[c0 + i] = u[i] * c + u[i + half] * s;", 0),
-    ("rope_cos_sin_swapped", "const double c = cos_t[m * half + i], s = sin_t[m * half + i];",
-     "const double c = sin_t[m * half + i], s = cos_t[m * half + i];", 0),
-    ("rope_adjacent_pairs", "orow[c0 + i + half] = u[i + half] * c + u[i] * s;",
-     "orow[c0 + i + half] = u[i + half] * c + u[(i + 1) % half] * s;", 0),
+    ("rope_sign", "orow[c0 + o + i] = u[o + i] * c - u[o + i + half] * s;",
+     "orow[c0 + o + i] = u[o + i] * c + u[o + i + half] * s;", 0),
+    ("rope_cos_sin_swapped", "const double c = cos_t[m * tab + o / 2 + i], s = sin_t[m * tab + o / 2 + i];",
+     "const double c = sin_t[m * tab + o / 2 + i], s = cos_t[m * tab + o / 2 + i];", 0),
+    ("rope_adjacent_pairs", "orow[c0 + o + i + half] = u[o + i + half] * c + u[o + i] * s;",
+     "orow[c0 + o + i + half] = u[o + i + half] * c + u[o + (i + 1) % half] * s;", 0),
+    # sections: every section reads the table from its first column; the section offset advances by
+    # half a width (dims and table columns confused); the sections are ignored (one split over rot)
+    ("rope_section_table_offset", "const double c = cos_t[m * tab + o / 2 + i], s = sin_t[m * tab + o / 2 + i];",
+     "const double c = cos_t[m * tab + i], s = sin_t[m * tab + i];", 0),
+    ("rope_section_offset_half", "        o += sec[j];\n", "        o += sec[j] / 2;\n", 0),
+    ("rope_sections_ignored", "  if (!sec) {\n    sec = one;", "  if (true) {\n    sec = one;", 0),
     ("rmsnorm_whole_width", "for (int64_t i = 0; i < hd; ++i) ss += yr[c0 + i] * yr[c0 + i];",
      "for (int64_t i = 0; i < qw; ++i) ss += yr[(c0 / qw) * qw + i] * yr[(c0 / qw) * qw + i];", 0),
     ("rmsnorm_eps_outside", "1.0 / std::sqrt(ss / static_cast<double>(hd) + eps)",

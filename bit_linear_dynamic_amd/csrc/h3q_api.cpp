@@ -324,28 +324,13 @@ h3q_status h3q_pack_weight(void* stream, const uint8_t* codes, const uint8_t* sc
   w->flags = flags;
   w->ts = tensor_scale;
   w->k_tiles = static_cast<int32_t>(w->K_pad / kGemmBK);
-  w->n_tiles = static_cast<int32_t>(gu ? (N / 2 + kGemmBN / 2 - 1) / (kGemmBN / 2) : (N + kGemmBN - 1) / kGemmBN);
+  w->n_tiles = static_cast<int32_t>(packed_n_tiles(N, gu));
 
-  // tile on the host: byte moves only (layout in h3q_kernels.hpp)
+  // tile on the host: byte moves only (layout in h3q_layout.hpp)
   const int64_t tiles = static_cast<int64_t>(w->n_tiles) * w->k_tiles;
   std::vector<uint32_t> tc(static_cast<size_t>(tiles * kCodeChunksPerTile * kGemmBN), 0u);
   std::vector<uint32_t> tsc(static_cast<size_t>(tiles * kGemmBN), 0u);
-  for (int64_t nt = 0; nt < w->n_tiles; ++nt)
-    for (int64_t c = 0; c < kGemmBN; ++c) {
-      const int64_t n = packed_row_source(nt, c, gu, N);
-      if (n < 0) continue;
-      const uint8_t* crow = codes + n * (K / 2);
-      const uint8_t* srow = scales + n * (K / 16);
-      for (int64_t kt = 0; kt < w->k_tiles; ++kt) {
-        const int64_t tile = nt * w->k_tiles + kt;
-        for (int64_t kc = 0; kc < kCodeChunksPerTile && kt * kGemmBK + kc * 8 < K; ++kc)
-          std::memcpy(&tc[(tile * kCodeChunksPerTile + kc) * kGemmBN + c], crow + (kt * kGemmBK + kc * 8) / 2, 4);
-        uint32_t sw = 0;
-        for (int64_t b = 0; b < kGemmBK / 16 && kt * (kGemmBK / 16) + b < K / 16; ++b)
-          sw |= static_cast<uint32_t>(srow[kt * (kGemmBK / 16) + b]) << (8 * b);
-        tsc[tile * kGemmBN + c] = sw;
-      }
-    }
+  tile_weight(codes, scales, N, K, gu, tc.data(), tsc.data());
   w->codes_bytes = tc.size() * 4;
   w->scales_bytes = tsc.size() * 4;
   (void)stream;  // synchronous copies: the caller's buffers are host memory
@@ -403,16 +388,8 @@ h3q_status h3q_register_adapter(h3q_weight w, int32_t id, const uint16_t* A, con
   a.alpha = alpha;
   const int64_t K = w->K, Kp = w->K_pad, N = w->N;
   std::vector<uint16_t> Ah(static_cast<size_t>(a.r_pad * Kp), 0);
-  for (int64_t j = 0; j < rank; ++j) std::memcpy(&Ah[j * Kp], A + j * K, K * sizeof(uint16_t));
-  const int64_t r_tiles = a.r_pad / kLoraBK;
-  std::vector<uint16_t> Bh(static_cast<size_t>(int64_t{w->n_tiles} * r_tiles * kGemmBN * kLoraBK), 0);
-  for (int64_t nt = 0; nt < w->n_tiles; ++nt)
-    for (int64_t c = 0; c < kGemmBN; ++c) {
-      const int64_t n = packed_row_source(nt, c, gate_up(w), N);
-      if (n < 0) continue;
-      for (int64_t j = 0; j < rank; ++j)
-        Bh[((nt * r_tiles + j / kLoraBK) * kGemmBN + c) * kLoraBK + j % kLoraBK] = B[n * rank + j];
-    }
+  std::vector<uint16_t> Bh(static_cast<size_t>(int64_t{w->n_tiles} * a.r_pad * kGemmBN), 0);
+  tile_adapter(A, B, rank, a.r_pad, N, K, Kp, gate_up(w), Ah.data(), Bh.data());
   h3q_status st = copy_to_device(reinterpret_cast<void**>(&a.A), Ah.data(), Ah.size() * 2);
   if (st == H3Q_OK) st = copy_to_device(reinterpret_cast<void**>(&a.B), Bh.data(), Bh.size() * 2);
   if (st != H3Q_OK) {

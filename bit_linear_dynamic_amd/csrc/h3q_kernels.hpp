@@ -6,21 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace h3q {
+#include "h3q_layout.hpp"
 
-// Tile geometry of the main GEMM and of the packed weight layout (see gemm_w4.hip).
-constexpr int kGemmBM = 256;   // rows of x per workgroup tile
-constexpr int kGemmBN = 256;   // output columns (packed weight rows) per workgroup tile
-constexpr int kGemmBK = 64;    // K per pipeline stage
-// Packed codes: for column tile nt and K-tile kt, chunk kc (8 consecutive k) of all 256 rows is one
-// run of 256 dwords: dword [((nt*k_tiles + kt)*8 + kc)*256 + c] holds row c's 8 codes, element i in
-// nibble i. Packed scales: dword [(nt*k_tiles + kt)*256 + c] holds row c's 4 E4M3 block scales.
-constexpr int kCodeChunksPerTile = kGemmBK / 8;          // 8
-constexpr int kCodeTileBytes = kCodeChunksPerTile * kGemmBN * 4;  // 8 KiB per (nt, kt)
-constexpr int kScaleTileBytes = kGemmBN * 4;              // 1 KiB per (nt, kt)
-// LoRA K-tiles are 32 deep (bf16 B and t' tiles of 16 KiB each fit the base tile's LDS stage).
-constexpr int kLoraBK = 32;
-constexpr int kLoraTileBytes = kGemmBN * kLoraBK * 2;     // 16 KiB per (nt, rank tile)
+namespace h3q {
 
 struct GemmParams {
   const uint16_t* act;      // bf16 [S][act_ld]: activation operand (x, x*pqs, or decoded NVFP4 x)
@@ -103,21 +91,6 @@ struct ActQuantParams {
   const float* xf = nullptr; // fp32 [S][K] input used as v instead of x * pqs (x, pqs unused), or null
 };
 hipError_t launch_act_quant(const ActQuantParams& p, hipStream_t stream);
-
-// Row of the caller's weight that row c of packed column tile nt holds, or -1 for padding.
-// Plain: nt*256 + c. Gate/up (F = N/2): the tile interleaves 32-row groups of gate rows
-// nt*128 + (c/64)*32 + c%32 and the matching up rows F + (same), so that one workgroup holds both
-// halves of every output column of SiLU(gate) * up.
-__host__ __device__ inline int64_t packed_row_source(int64_t nt, int64_t c, bool gate_up, int64_t N) {
-  if (!gate_up) {
-    const int64_t n = nt * kGemmBN + c;
-    return n < N ? n : -1;
-  }
-  const int64_t F = N / 2;
-  const int64_t j = nt * (kGemmBN / 2) + (c / 64) * 32 + (c % 32);
-  if (j >= F) return -1;
-  return ((c / 32) % 2) ? F + j : j;
-}
 
 struct DequantParams {
   const uint32_t* wcodes_dw;

@@ -12,17 +12,22 @@
 // RTM = ceil(bm / 32) row tiles of 32 (rows of the last tile past bm read as zero and are not
 // written). Every wave computes all RTM row tiles for its columns: the r_pad/32 column tiles of 32
 // go to the waves round-robin, at most NC per wave, as RTM x NC tiles of v_mfma_f32_32x32x16_bf16.
-// x is read once from HBM, so this is a streaming kernel: K is staged BK (64, or 32 when the A tile
-// is large) at a time through as many LDS stages as fit (up to 8) by buffer->LDS copies of the x
-// tile (RTM*32 x BK), the A tile (r_pad x BK) and BK pqs values, and the global latency is hidden by
-// the bytes in flight rather than by compute. Each wave waits for its own copies with one vmcnt and
-// a barrier hands the stage over. The waves also write xs = bf16(x * pqs), reading the tile back
-// from LDS row by row so that every store covers whole 128-byte row segments (8 rows per store of a
-// wave; stores of 32-byte pieces of 32 rows, straight from the MFMA operand registers, ran the write
-// stream at a fraction of the read rate). Every vector-memory operation of the K loop is issued by
-// the asm helpers of h3q_device.hpp in a fixed number per wave per tile (copies without a real
-// source re-read into a spare LDS area, stores without a real target go past the buffer's end and
-// are dropped), so one vmcnt value per iteration waits exactly for the tile about to be read.
+//
+// x is read once from HBM, so this is a streaming kernel bound by how many x bytes are in flight per
+// CU. K goes through in BK-deep tiles (64, or 32 when each wave holds more than one column tile) on
+// two separate rings of LDS slots, both filled by buffer->LDS copies (no registers): the adapter tile
+// A (r_pad x BK, from L2, where every workgroup reads it) one tile ahead in two slots, and the x tile
+// (RTM*32 x BK) with its BK pqs values L tiles ahead in L + 2 slots -- all the LDS the two A slots
+// leave is x in flight (80 KiB at r = 384 and at r = 128, against 30 and 60 KiB when every stage held
+// an A tile and its x tile). Each step issues the A tile first and the x tile after it, so waiting
+// for the A tile it is about to read never waits for the x tiles behind it; the x tile it reads is
+// older than that A tile, so it has landed too. One vmcnt value per step parity and a barrier hand
+// the slots over. xs = bf16(x * pqs) is written from the LDS copy of each 64-deep tile, or of two
+// 32-deep tiles after the second, so that each 16-byte store is one chunk of a 128-byte row segment
+// and a wave's store covers 8 whole segments.
+// Every vector-memory operation of the K loop is issued by the asm helpers of h3q_device.hpp in a
+// fixed number per wave (copies without a real source go to a spare LDS area, stores without a real
+// target go past the buffer's end and are dropped), so the counts behind each vmcnt are exact.
 //
 // Prescale: the elementwise xs = bf16(x * pqs) on its own, for calls without an adapter.
 #include <algorithm>
@@ -37,36 +42,49 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxRTM = 6;
-constexpr uint32_t kLdsBudget = 150 * 1024;
-
-// Stage bytes for K-tiles of depth bk: x tile, A tile, pqs (256 B), 1 KiB target of padding copies.
-constexpr uint32_t ld_stage_bytes(int rtm, int nc, int bk) {
-  return static_cast<uint32_t>(rtm * 32 * bk * 2 + 4 * nc * 32 * bk * 2 + 256 + 1024);
-}
+constexpr uint32_t kLdsBudget = 160 * 1024;
+constexpr int kMaxAhead = 10;            // x tiles in flight at most
 
 template <int RTM, int NC>
 struct LdGeo {
-  // 64-deep tiles (128-byte row segments) when three stages of them fit, else 32-deep
-  static constexpr int BK = 3 * ld_stage_bytes(RTM, NC, 64) <= kLdsBudget ? 64 : 32;
-  static constexpr int CT = 4 * NC;                      // column tiles the A stage is sized for
-  static constexpr uint32_t kX = 0;                      // x tile: RTM*32 rows x 2*BK bytes
-  static constexpr uint32_t kA = RTM * 32 * BK * 2;      // A tile: CT*32 rows x 2*BK bytes
-  static constexpr uint32_t kP = kA + CT * 32 * BK * 2;  // BK pqs values
-  static constexpr uint32_t kSpare = kP + 256;           // 1 KiB target of padding copies
-  static constexpr uint32_t kStage = kSpare + 1024;
-  static constexpr int kStagesFit = static_cast<int>(kLdsBudget / kStage);
-  static constexpr int kStages = kStagesFit < 8 ? kStagesFit : 8;
-  static constexpr int L = kStages - 1;                  // tiles in flight ahead of the one read
-  static constexpr uint32_t kLds = kStages * kStage;
-  static constexpr int kCopiesX = (RTM * BK / 16 + 3) / 4;  // 1 KiB copies per wave (RTM*BK/16 per tile)
-  static constexpr int kCopiesA = NC * BK / 16;             // (at most CT*BK/16 per tile)
-  static constexpr int kPqsLanes = BK / 16;                 // 16 bytes each, per wave
-  static constexpr int CPT = kCopiesX + kCopiesA + 1;
-  static constexpr int kChunks = RTM * 32 * (BK / 8);       // 16-byte xs chunks per tile
-  static constexpr int NS = (kChunks + 255) / 256;          // xs stores per wave per tile
-  static_assert(ld_stage_bytes(RTM, NC, BK) == kStage, "stage layout");
-  static_assert(kStages >= 3, "at least two tiles in flight");
-  static_assert((L - 1) * CPT + L * NS < 64, "vmcnt range");
+  // K per tile: 64 (128-byte row segments of x and xs) when the adapter tile is small (one column
+  // tile per wave), else 32, which leaves room for more x tiles in flight beside the two A tiles.
+  // (Measured at S = 37726: r = 384 0.374 -> 0.301 ms against A staged as deep as x; 32-deep tiles
+  // at r = 128 were 3-7 % slower than 64-deep ones, and a second A tile ahead at r = 384, which takes
+  // two x tiles out of flight, was 20 % slower.)
+  static constexpr int BK = NC == 1 ? 64 : 32;
+  static constexpr int LA = 1;                                // A tiles issued ahead
+  static constexpr int NA = LA + 1;                           // A slots
+  static constexpr int CT = 4 * NC;                           // column tiles the A slots hold
+  static constexpr uint32_t kASlot = CT * 32 * BK * 2;        // A tile: CT*32 rows x 2*BK bytes
+  static constexpr uint32_t kXTile = RTM * 32 * BK * 2;       // x tile: RTM*32 rows x 2*BK bytes
+  static constexpr uint32_t kXSlot = kXTile + BK * 4;         // + the tile's pqs values
+  static constexpr uint32_t kSpare = NA * kASlot;             // 1 KiB target of copies without a source
+  static constexpr uint32_t kX0 = kSpare + 1024;              // first x slot
+  static constexpr int kCX = (RTM * BK / 16 + 3) / 4;         // 1 KiB x copies per wave (RTM*BK/16 per tile)
+  static constexpr int kCA = NC * BK / 16;                    // 1 KiB A copies per wave (CT*BK/16 per tile)
+  static constexpr int kXOps = kCX + 1;                       // + one pqs copy (BK/16 lanes per wave)
+  // xs stores per wave: 64-deep tiles store each tile (RTM per step); 32-deep tiles store two tiles
+  // at once after the odd step, so that every store is a chunk of a 128-byte row segment
+  static constexpr int kStEven = BK == 64 ? RTM : 0, kStOdd = RTM;
+  static constexpr int kFit = static_cast<int>((kLdsBudget - kX0) / kXSlot) - 2;
+  // Operations a wave can have in flight: LA A tiles, L x tiles, two xs store rounds; kept below 64
+  // so that every count stays within the vmcnt field.
+  static constexpr int kVm = (63 - LA * kCA - 2 * RTM) / kXOps;
+  static constexpr int kL0 = kFit < kVm ? kFit : kVm;
+  static constexpr int L = kL0 < kMaxAhead ? kL0 : kMaxAhead;  // x tiles issued ahead
+  static constexpr int NX = L + 2;                            // x slots: L in flight, 2 being read
+  static constexpr uint32_t kLds = kX0 + NX * kXSlot;
+  static_assert(L > LA, "x tiles must be issued further ahead than A tiles");
+  static_assert(kLds <= kLdsBudget, "LDS");
+  static_assert(LA * kCA + L * kXOps + 2 * RTM < 64, "vmcnt range");
+  // vmcnt to wait for A tile kt at the top of step kt: everything issued after it -- the x tile
+  // that step kt - 1 issued after A(kt) and that step's xs stores (none without an xs output);
+  static constexpr int wait_steady(int parity, bool xs) {  // parity of kt
+    return kXOps + (xs ? (parity ? kStEven : kStOdd) : 0);
+  }
+  // at step 0, the x tiles 1 .. L - 1 that the prologue issued after A(0).
+  static constexpr int wait_first0 = (L - 1) * kXOps;
 };
 
 // Loads 8 bf16 of x at (row, k) -- zeros past K (K is a multiple of 16, so chunks never straddle).
@@ -118,97 +136,158 @@ __device__ __forceinline__ uint32_t copy_src_column(uint32_t q, uint32_t lane) {
   else return (cl & 3) * 8;
 }
 
-// A per-lane offset past the end of the x descriptor (which spans under 2^31 bytes): the copy reads
-// zeros. Adding the tile's column offset (under 2^21 bytes) cannot wrap it past 2^32.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
 template <int BK>
 __device__ __forceinline__ uint32_t tile_offset(uint32_t row, uint32_t chunk) {
   if constexpr (BK == 64) return lds_chunk_offset(row, chunk);
   else return lds_chunk_offset32(row, chunk);
 }
 
+// A per-lane offset past the end of the x descriptor (which spans under 2^31 bytes): the copy reads
+// zeros. Adding the tile's column offset (under 2^21 bytes) cannot wrap it past 2^32.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 struct LdCtx {
   u32x4 x, A, pq, xs;
-  uint32_t x_row_bytes, A_row_bytes;
+  uint32_t x_row_bytes, A_row_bytes, xs_row_bytes;
   uint32_t K;
   uint32_t wave, lane;
-  int k_tiles, x_copies, A_copies;  // real copies per tile for the whole workgroup
+  int k_tiles, x_copies;  // real x copies per tile for the whole workgroup
+  uint32_t smem0;
 };
 
-// Issues this wave's copies of K-tile kt (a re-read of the last tile when kt is past the end).
+// This wave's copies of A tile kt into A slot `slot` (to the spare area past the last tile).
 template <int RTM, int NC>
-__device__ __forceinline__ void issue_tile(const LdCtx& c, int kt, uint32_t stage) {
+__device__ __forceinline__ void issue_A(const LdCtx& c, int kt, int slot) {
+  using G = LdGeo<RTM, NC>;
+  const bool real = kt < c.k_tiles;
+  const uint32_t k0 = static_cast<uint32_t>(real ? kt : 0) * G::BK;
+#pragma unroll
+  for (int i = 0; i < G::kCA; ++i) {
+    const uint32_t q = c.wave + 4 * i;
+    dma16(c.A, c.smem0 + (real ? slot * G::kASlot + q * 1024 : G::kSpare),
+          copy_src_offset<G::BK>(q, c.lane, c.A_row_bytes), k0 * 2);
+  }
+}
+
+// This wave's copies of x tile kt and its pqs values into x slot `slot` (to the spare area past the
+// last tile).
+template <int RTM, int NC>
+__device__ __forceinline__ void issue_x(const LdCtx& c, int kt, int slot) {
   using G = LdGeo<RTM, NC>;
   constexpr int BK = G::BK;
-  const uint32_t k0 = static_cast<uint32_t>(kt < c.k_tiles ? kt : c.k_tiles - 1) * BK;
+  const bool tile = kt < c.k_tiles;
+  const uint32_t k0 = static_cast<uint32_t>(tile ? kt : 0) * BK;
+  const uint32_t base = c.smem0 + G::kX0 + static_cast<uint32_t>(slot) * G::kXSlot;
 #pragma unroll
-  for (int i = 0; i < G::kCopiesX; ++i) {
+  for (int i = 0; i < G::kCX; ++i) {
     const uint32_t q = c.wave + 4 * i;
-    const bool real = static_cast<int>(q) < c.x_copies;
+    const bool real = tile && static_cast<int>(q) < c.x_copies;
     const uint32_t qs = real ? q : 0;
     // x rows are K elements apart, so the 16 bytes past a row's end are the next row's first
     // elements: columns at or past K read as zero instead (A is zero there, but 0 * inf is not 0).
     const uint32_t voff = k0 + copy_src_column<BK>(qs, c.lane) < c.K ? copy_src_offset<BK>(qs, c.lane, c.x_row_bytes)
-                                                                    : kOutOfRange;
-    dma16(c.x, stage + (real ? G::kX + q * 1024 : G::kSpare), voff, k0 * 2);
+                                                                     : kOutOfRange;
+    dma16(c.x, real ? base + q * 1024 : c.smem0 + G::kSpare, voff, k0 * 2);
   }
-#pragma unroll
-  for (int i = 0; i < G::kCopiesA; ++i) {
-    const uint32_t q = c.wave + 4 * i;
-    const bool real = static_cast<int>(q) < c.A_copies;
-    dma16(c.A, stage + (real ? G::kA + q * 1024 : G::kSpare), copy_src_offset<BK>(real ? q : 0, c.lane, c.A_row_bytes),
-          k0 * 2);
-  }
-  dma16_lanes<G::kPqsLanes>(c.pq, stage + G::kP + c.wave * (BK * 1), c.lane * 16, k0 * 4 + c.wave * (BK * 1));
+  // the tile's BK pqs values: lanes 0 .. BK/16 - 1 of every wave copy BK bytes
+  dma16_lanes<BK / 16>(c.pq, tile ? base + G::kXTile + c.wave * BK : c.smem0 + G::kSpare, c.lane * 16,
+                       k0 * 4 + c.wave * BK);
 }
 
-// Waits for tile kt: newer than its copies are those of the L - 1 tiles after it and the xs
-// stores of the min(kt, L) iterations since it was issued.
-template <int L, int CPT, int NS>
-__device__ __forceinline__ void wait_tile(int kt) {
-  switch (kt < L ? kt : L) {
-    case 0: stage_barrier<(L - 1) * CPT>(); break;
-    case 1: stage_barrier<(L - 1) * CPT + 1 * NS>(); break;
-    case 2: stage_barrier<(L - 1) * CPT + 2 * NS>(); break;
-    case 3: stage_barrier<(L - 1) * CPT + 3 * NS>(); break;
-    case 4: stage_barrier<(L - 1) * CPT + 4 * NS>(); break;
-    case 5: stage_barrier<(L - 1) * CPT + 5 * NS>(); break;
-    case 6: stage_barrier<(L - 1) * CPT + 6 * NS>(); break;
-    default: stage_barrier<(L - 1) * CPT + 7 * NS>(); break;
+// The MFMAs of one tile: x operand from x slot xb, A operand from A slot ab.
+template <int RTM, int NC>
+__device__ __forceinline__ void mfma_tile(f32x16 (&acc)[RTM][NC], const uint8_t* xb, const uint8_t* ab,
+                                          uint32_t wave, uint32_t r32, uint32_t h32) {
+  constexpr int BK = LdGeo<RTM, NC>::BK;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    // Column tile jt = wave + 4j is always inside the A slot (CT = 4 NC tiles); a tile at or past ct
+    // holds zeros (rows past r_pad read as zero) and its accumulator is never stored. No branch: with
+    // one, the compiler moved the accumulators between AGPRs and VGPRs around every MFMA.
+    bf16x8 a[RTM], b[NC];
+#pragma unroll
+    for (int i = 0; i < RTM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(xb + tile_offset<BK>(i * 32 + r32, kk * 2 + h32));
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const uint32_t jt = wave + 4 * j;
+      b[j] = *reinterpret_cast<const bf16x8*>(ab + tile_offset<BK>(jt * 32 + r32, kk * 2 + h32));
+    }
+#pragma unroll
+    for (int i = 0; i < RTM; ++i)
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// xs = bf16(x * pqs) of 64 columns from the LDS copies of the x tile(s) -- columns [64 kp, 64 kp + 64)
+// -- row-major: chunk q of the workgroup (16 bytes) is row q / 8, chunk q % 8 of the 128-byte row
+// segment, so one store of a wave covers 8 whole segments. With 32-deep tiles chunks 0..3 come from
+// the tile in slot x0 and chunks 4..7 from the next tile in slot x1; with 64-deep tiles all from x0.
+// A lane's chunks all sit at the same 8 columns, so its pqs values are read once; all RTM chunks are
+// read before the first store. Rows past the workgroup's rows go past the buffer's end and are
+// dropped; columns past K are zero (x and pqs read as zero there).
+template <int RTM, int NC>
+__device__ __forceinline__ void xs_store(const LdCtx& c, const uint8_t* x0, const uint8_t* x1, int kp, bool has_pqs) {
+  using G = LdGeo<RTM, NC>;
+  constexpr int BK = G::BK;
+  const uint32_t cc = c.lane & 7;
+  const uint8_t* xb = (BK == 64 || cc < 4) ? x0 : x1;
+  const uint32_t ch = BK == 64 ? cc : (cc & 3);
+  float ps[8];
+  if (has_pqs) {
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(xb + G::kXTile + ch * 32);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(xb + G::kXTile + ch * 32 + 16);
+    ps[0] = q0.x; ps[1] = q0.y; ps[2] = q0.z; ps[3] = q0.w;
+    ps[4] = q1.x; ps[5] = q1.y; ps[6] = q1.z; ps[7] = q1.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ps[e] = 1.0f;
+  }
+  u32x4 xv[RTM];
+#pragma unroll
+  for (int q = 0; q < RTM; ++q) {
+    const uint32_t row = (c.wave * 64 + c.lane + 256u * q) >> 3;
+    xv[q] = *reinterpret_cast<const u32x4*>(xb + tile_offset<BK>(row, ch));
+  }
+#pragma unroll
+  for (int q = 0; q < RTM; ++q) {
+    const uint32_t row = (c.wave * 64 + c.lane + 256u * q) >> 3;
+    buf_store16(scale_chunk(xv[q], ps), c.xs, row * c.xs_row_bytes + cc * 16, static_cast<uint32_t>(kp) * 128);
   }
 }
 
 template <int RTM, int NC, bool XS>
 __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p) {
   using G = LdGeo<RTM, NC>;
-  constexpr int L = G::L, CPT = G::CPT, NS = XS ? G::NS : 0, NST = G::kStages, BK = G::BK;
-  static_assert(L <= 7, "wait_tile covers up to 7 tiles in flight");
+  constexpr int BK = G::BK, L = G::L, LA = G::LA, NX = G::NX, NA = G::NA;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * p.bm;
   const int64_t rows = std::min<int64_t>(p.bm, p.S - m0);  // <= 32 * RTM
-  const int ct = p.r_pad / 32;  // column tiles: wave w owns tiles w, w + 4, ... (< ct)
 
   LdCtx c;
   c.wave = wave;
   c.lane = lane;
-  // K_pad / BK tiles (K_pad is a multiple of 64): with 32-deep tiles that can be one tile past
-  // ceil(K / BK), whose x columns are all padding, so xs is written with zeros out to K_pad -- the
-  // GEMM reads K_pad columns of it, and the workspace holds whatever an earlier call left there.
+  // K_pad / BK tiles (K_pad is a multiple of 64: the count is even for 32-deep tiles and may be odd
+  // for 64-deep ones): xs is written with zeros out to K_pad -- the GEMM reads K_pad columns of it,
+  // and the workspace holds whatever an earlier call left there.
   c.k_tiles = static_cast<int>(p.K_pad / BK);
   c.K = static_cast<uint32_t>(p.K);
   c.x_copies = RTM * BK / 16;
-  c.A_copies = ct * BK / 16;
   c.x_row_bytes = static_cast<uint32_t>(p.K * 2);
   c.A_row_bytes = static_cast<uint32_t>(p.K_pad * 2);
+  c.xs_row_bytes = static_cast<uint32_t>(p.K_pad * 2);
   c.x = buf_rsrc(p.x + m0 * p.K, static_cast<uint32_t>(rows * p.K * 2));
   c.A = buf_rsrc(p.A, static_cast<uint32_t>(int64_t{p.r_pad} * p.K_pad * 2));
   c.pq = buf_rsrc(p.pqs, p.pqs ? static_cast<uint32_t>(p.K * 4) : 0u);
-  c.xs = buf_rsrc(p.xs_out + m0 * p.K_pad,
-                  XS ? static_cast<uint32_t>(rows * p.K_pad * 2) : 0u);
+  c.xs = buf_rsrc(p.xs_out + m0 * p.K_pad, XS ? static_cast<uint32_t>(rows * p.K_pad * 2) : 0u);
+  c.smem0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(smem)));
+  const bool has_pqs = p.pqs != nullptr;
 
   f32x16 acc[RTM][NC];
 #pragma unroll
@@ -216,93 +295,67 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
 #pragma unroll
     for (int j = 0; j < NC; ++j) acc[i][j] = f32x16{};
 
-  const uint32_t smem0 = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(smem)));
   const uint32_t r32 = lane & 31, h32 = lane >> 5;
+  const uint8_t* xslot0 = smem + G::kX0;
 
+  // Prologue: x(0), A(0), then x(1) .. x(L - 1): every A tile follows the x tile of the same index,
+  // so waiting for an A tile also waits for its x tile.
+  issue_x<RTM, NC>(c, 0, 0);
+  issue_A<RTM, NC>(c, 0, 0);
 #pragma unroll
-  for (int t = 0; t < L; ++t) issue_tile<RTM, NC>(c, t, smem0 + t * G::kStage);
-  int s_cur = 0;
-  // Not unrolled: unrolled by the stage count, some shapes had their accumulators moved between
-  // AGPRs and VGPRs hundreds of times per tile and ran at a third of the copy rate.
+  for (int t = 1; t < L; ++t) issue_x<RTM, NC>(c, t, t);
+
+  // Step kt reads x slot kt % NX and A slot kt % 2; it first issues A tile kt + 1 into the A slot
+  // read at step kt - 1, then x tile kt + L into x slot (kt + L) % NX, that of tile kt - 2, whose
+  // MFMAs and xs stores were issued before the barrier that opened step kt - 1 or kt.
+  int sx = 0, sa = 0;  // kt % NX, kt % NA
+  // Steps go in pairs (even, odd) so that each wait count is a constant; the pair loop is not
+  // unrolled further: unrolled by the stage count, some shapes had their accumulators moved between
+  // AGPRs and VGPRs hundreds of times per tile.
+  int kt = 0;
 #pragma unroll 1
-  for (int kt = 0; kt < c.k_tiles; ++kt) {
-    wait_tile<L, CPT, NS>(kt);
-    const int s_iss = s_cur == 0 ? NST - 1 : s_cur - 1;  // (kt + L) % NST: the stage of tile kt - 1
-    issue_tile<RTM, NC>(c, kt + L, smem0 + s_iss * G::kStage);
-    const uint8_t* st = smem + s_cur * G::kStage;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      // Column tile jt = wave + 4j is always inside the stage's A area (CT = 4 NC tiles); a tile at or
-      // past ct holds no copy of A, and its accumulator is computed but never stored. No branch: with
-      // one, the compiler moved the accumulators between AGPRs and VGPRs around every MFMA.
-      bf16x8 a[RTM], b[NC];
-#pragma unroll
-      for (int i = 0; i < RTM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(st + G::kX + tile_offset<BK>(i * 32 + r32, kk * 2 + h32));
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int jt = static_cast<int>(wave) + 4 * j;
-        b[j] = *reinterpret_cast<const bf16x8*>(st + G::kA + tile_offset<BK>(jt * 32 + r32, kk * 2 + h32));
-      }
-#pragma unroll
-      for (int i = 0; i < RTM; ++i)
-#pragma unroll
-        for (int j = 0; j < NC; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+  for (; kt + 1 < c.k_tiles; kt += 2) {
+    const int sx1 = sx + 1 == NX ? 0 : sx + 1;
+    const int sa1 = sa + 1 == NA ? 0 : sa + 1;
+    const int sal = sa + LA >= NA ? sa + LA - NA : sa + LA;     // (kt + LA) % NA
+    const int sal1 = sa1 + LA >= NA ? sa1 + LA - NA : sa1 + LA;
+    const int sxl = sx + L >= NX ? sx + L - NX : sx + L;         // (kt + L) % NX
+    const int sxl1 = sxl + 1 == NX ? 0 : sxl + 1;
+    // even step kt
+    if (kt == 0) stage_barrier<G::wait_first0>();
+    else stage_barrier<G::wait_steady(0, XS)>();
+    issue_A<RTM, NC>(c, kt + LA, sal);
+    issue_x<RTM, NC>(c, kt + L, sxl);
+    mfma_tile<RTM, NC>(acc, xslot0 + sx * G::kXSlot, smem + sa * G::kASlot, wave, r32, h32);
+    if constexpr (XS && BK == 64) xs_store<RTM, NC>(c, xslot0 + sx * G::kXSlot, nullptr, kt, has_pqs);
+    // odd step kt + 1
+    stage_barrier<G::wait_steady(1, XS)>();
+    issue_A<RTM, NC>(c, kt + 1 + LA, sal1);
+    issue_x<RTM, NC>(c, kt + 1 + L, sxl1);
+    mfma_tile<RTM, NC>(acc, xslot0 + sx1 * G::kXSlot, smem + sa1 * G::kASlot, wave, r32, h32);
     if constexpr (XS) {
-      // xs = bf16(x * pqs) of the whole tile from its LDS copy, row-major: chunk q of the workgroup
-      // (16 bytes) is row q / (BK/8), chunk q % (BK/8), so one store of a wave covers 8 (BK = 64) or
-      // 16 (BK = 32) rows of full row segments. A lane's chunks all sit at the same column
-      // (lane % (BK/8)), so its 8 pqs values are read once; all NS chunks are read before the first
-      // store, so the LDS latency is paid once. Every wave issues NS stores; chunks past the tile go
-      // past the buffer's end and are dropped.
-      constexpr bool kAllReal = G::kChunks % 256 == 0;
-      const uint32_t cc = lane % (BK / 8);
-      float ps[8];
-      if (p.pqs) {
-        const f32x4 q0 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32);
-        const f32x4 q1 = *reinterpret_cast<const f32x4*>(st + G::kP + cc * 32 + 16);
-        ps[0] = q0.x; ps[1] = q0.y; ps[2] = q0.z; ps[3] = q0.w;
-        ps[4] = q1.x; ps[5] = q1.y; ps[6] = q1.z; ps[7] = q1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ps[e] = 1.0f;
-      }
-      u32x4 xv[NS];
-#pragma unroll
-      for (int q = 0; q < NS; ++q) {
-        const uint32_t row = (wave * 64 + lane + 256u * q) / (BK / 8);
-        const bool real = kAllReal || static_cast<int>(wave * 64 + lane + 256u * q) < G::kChunks;
-        xv[q] = real ? *reinterpret_cast<const u32x4*>(st + G::kX + tile_offset<BK>(row, cc)) : u32x4{0u, 0u, 0u, 0u};
-      }
-      if (static_cast<int64_t>(kt + 1) * BK > p.K) {  // the last tile: padding columns become zero
-        const bool pad = static_cast<uint32_t>(kt) * BK + cc * 8 >= p.K;
-#pragma unroll
-        for (int q = 0; q < NS; ++q)
-          if (pad) xv[q] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (pad) ps[e] = 1.0f;
-      }
-#pragma unroll
-      for (int q = 0; q < NS; ++q) {
-        const uint32_t chunk = wave * 64 + lane + 256u * q;
-        const bool real = kAllReal || static_cast<int>(chunk) < G::kChunks;
-        const u32x4 out = scale_chunk(xv[q], ps);
-        // (the dummy offset stays out of range with the tile's column offset added: < 2^31 + 2^21)
-        buf_store16(out, c.xs, real ? (chunk / (BK / 8)) * static_cast<uint32_t>(p.K_pad * 2) + cc * 16 : 0x7ffffff0u,
-                    static_cast<uint32_t>(kt) * BK * 2);
-      }
+      if constexpr (BK == 64) xs_store<RTM, NC>(c, xslot0 + sx1 * G::kXSlot, nullptr, kt + 1, has_pqs);
+      else xs_store<RTM, NC>(c, xslot0 + sx * G::kXSlot, xslot0 + sx1 * G::kXSlot, kt / 2, has_pqs);
     }
-    s_cur = s_cur == NST - 1 ? 0 : s_cur + 1;
+    sx = sx1 + 1 == NX ? 0 : sx1 + 1;
+    sa = sa1 + 1 == NA ? 0 : sa1 + 1;
+  }
+  if constexpr (BK == 64) {
+    // an odd number of 64-deep tiles (K_pad / 64 is odd): the last one is an even step on its own;
+    // nothing is issued after it
+    if (kt < c.k_tiles) {
+      if (kt == 0) stage_barrier<G::wait_first0>();
+      else stage_barrier<G::wait_steady(0, XS)>();
+      mfma_tile<RTM, NC>(acc, xslot0 + sx * G::kXSlot, smem + sa * G::kASlot, wave, r32, h32);
+      if constexpr (XS) xs_store<RTM, NC>(c, xslot0 + sx * G::kXSlot, nullptr, kt, has_pqs);
+    }
   }
   wait_vmcnt<0>();  // drain the trailing copies and stores before the workgroup can end
 
   const float f = p.f_div_dev ? p.f / *p.f_div_dev : p.f;
   const int row_lane = (lane >> 5) * 4;
   const int R = p.r_pad;
+  const int ct = p.r_pad / 32;  // column tiles: wave w owns tiles w, w + 4, ... (< ct)
 #pragma unroll
   for (int i = 0; i < RTM; ++i)
 #pragma unroll

@@ -726,9 +726,11 @@ h3q_status h3q_merge_adapter(void* stream_, h3q_weight w, int32_t adapter_id, fl
   int dev;
   if (h3q_status st = check_device(&dev)) return st;
   if (dev != w->device) return fail(H3Q_E_ARG, "merge_adapter: weight lives on device %d, current is %d", w->device, dev);
+  // the weight's lock is held until the merge has finished on the device, so that the adapter's
+  // buffers cannot be unregistered (freed) while its kernels read them
+  std::lock_guard<std::mutex> lk(w->mu);
   Adapter ad;
   if (adapter_id != H3Q_ADAPTER_NONE) {
-    std::lock_guard<std::mutex> lk(w->mu);
     auto it = w->adapters.find(adapter_id);
     if (it == w->adapters.end()) return fail(H3Q_E_ADAPTER, "merge_adapter: unknown adapter id %d", adapter_id);
     ad = it->second;  // device buffers stay owned by the handle
@@ -840,16 +842,18 @@ h3q_status h3q_timing_enable(int32_t on) {
 h3q_status h3q_timing_get(int32_t kind, double* total_ms, int64_t* launches) {
   if (kind < 0 || kind > 3 || !total_ms || !launches) return fail(H3Q_E_ARG, "timing_get: bad kind or null pointer");
   std::lock_guard<std::mutex> lk(g_timing.mu);
-  for (auto& r : g_timing.pending) {
+  // records leave the pending list as they are counted, so a failure part-way counts none twice
+  while (!g_timing.pending.empty()) {
+    const TimingRec r = g_timing.pending.back();
     float ms = 0.0f;
     H3Q_HIP_TRY(hipEventSynchronize(r.end));
     H3Q_HIP_TRY(hipEventElapsedTime(&ms, r.begin, r.end));
+    g_timing.pending.pop_back();
     g_timing.ms[r.kind] += ms;
     g_timing.launches[r.kind] += 1;
     g_timing.pool.push_back(r.begin);
     g_timing.pool.push_back(r.end);
   }
-  g_timing.pending.clear();
   *total_ms = g_timing.ms[kind];
   *launches = g_timing.launches[kind];
   g_timing.ms[kind] = 0.0;

@@ -415,3 +415,37 @@ def test_w4a4_linear_parity(S, K, N, gate_up):
                 assert normwise(h, oracle.swiglu(ref)) <= TOL
     finally:
         p.free()
+
+
+def test_timing_counts_launches_per_kernel():
+    """The per-kernel timing behind the benchmark's breakdown: each call records one launch of each
+    kernel it runs, a read returns and clears that kernel's totals, and nothing is recorded while
+    timing is off."""
+    S, K, N = 200, 512, 512
+    say("timing counts")
+    p = Proj(N, K, 1700)
+    try:
+        p.add_adapter(1, 32, 32.0, 1701, 1702)
+        x = dev(synth.activation(S, K, 1703))
+        pqs = dev(synth.pre_quant_scale(K, 1704))
+        kinds = (h3q.H3Q_KERNEL_GEMM, h3q.H3Q_KERNEL_LORA_DOWN, h3q.H3Q_KERNEL_PRESCALE, h3q.H3Q_KERNEL_ACT_QUANT)
+        h3q.h3q_timing_enable(False)
+        h3q.h3q_linear_ex(x, pqs, p.handle, 1, 1.0, 0)
+        h3q.h3q_timing_enable(True)
+        for _ in range(3):
+            h3q.h3q_linear_ex(x, pqs, p.handle, 1, 1.0, 0)                      # LoRA-down + GEMM
+        for _ in range(2):
+            h3q.h3q_linear_ex(x, pqs, p.handle, h3q.H3Q_ADAPTER_NONE, 0.0, 0)   # prescale + GEMM
+        h3q.h3q_linear_ex(x, pqs, p.handle, h3q.H3Q_ADAPTER_NONE, 0.0, h3q.H3Q_ACT_NVFP4)  # act-quant + GEMM
+        torch.cuda.synchronize()
+        got = {k: h3q.h3q_timing_get(k) for k in kinds}
+        assert [got[k][1] for k in kinds] == [6, 3, 2, 1], got
+        assert all(got[k][0] > 0.0 for k in kinds), got
+        assert h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM) == (0.0, 0)  # read clears
+        h3q.h3q_timing_enable(False)
+        h3q.h3q_linear_ex(x, pqs, p.handle, 1, 1.0, 0)
+        torch.cuda.synchronize()
+        assert h3q.h3q_timing_get(h3q.H3Q_KERNEL_GEMM) == (0.0, 0)
+    finally:
+        h3q.h3q_timing_enable(False)
+        p.free()

@@ -33,6 +33,8 @@ __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 // them, so it keeps kAmaxRows independent loads in flight and reads its pqs values once per column.
 // (One load per thread at a time, a row at a time, streamed x at ~2 TB/s.)
 constexpr int kAmaxRows = 8;
+// Grid cap of both passes (their loops stride over the grid, so any size gives the same result).
+constexpr int64_t kMaxGrid = int64_t{1} << 20;
 
 __global__ __launch_bounds__(256) void amax_kernel(ActQuantParams p) {
   float m = 0.0f;
@@ -80,9 +82,14 @@ __global__ __launch_bounds__(256) void amax_kernel(ActQuantParams p) {
       }
     }
   }
-  // wave64 reduction, then one atomic per wave (|v| >= 0: fp32 bit patterns order as unsigned)
+  // wave64 reduction, the four waves through LDS, then one atomic per workgroup (|v| >= 0: fp32 bit
+  // patterns order as unsigned)
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(p.amax_bits, __float_as_uint(m));
+  __shared__ float wave_max[4];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(p.amax_bits, __float_as_uint(fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]))));
 }
 
 __device__ __forceinline__ float tensor_scale(uint32_t amax_bits) {
@@ -191,14 +198,16 @@ hipError_t launch_act_quant(const ActQuantParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.S > 0) {
+    // one row block per workgroup: a grid-stride loop over fewer workgroups left its last round
+    // partly empty (2.3 rounds of 2048 workgroups at S = 37726: 3.6 TB/s)
     const int64_t blocks = (p.S + kAmaxRows - 1) / kAmaxRows;
-    const int64_t grid = blocks < 256 * 8 ? blocks : 256 * 8;  // one or more row blocks per workgroup
+    const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
     hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  int64_t grid = (p.S * (p.K / 16) + 255) / 256;
+  int64_t grid = (p.S * (p.K / 16) + 255) / 256;  // one 16-block per thread where the grid allows
   if (grid < 1) grid = 1;
-  if (grid > 256 * 64) grid = 256 * 64;
+  if (grid > kMaxGrid) grid = kMaxGrid;
   hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

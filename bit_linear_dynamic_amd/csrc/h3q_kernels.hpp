@@ -67,6 +67,7 @@ struct LoraDownParams {
   uint16_t* t_out;          // bf16 [S][r_pad]
   uint16_t* xs_out;         // bf16 [S][K_pad] = x * pqs, or null
   int64_t bm;               // rows per workgroup (set by launch_lora_down)
+  int32_t groups;           // column groups of A per row block (set by launch_lora_down)
 };
 hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream);
 

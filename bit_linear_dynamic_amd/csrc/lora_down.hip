@@ -7,11 +7,14 @@
 // The same pass writes the base path's operand xs = bf16(x * pqs) (same section: pre_quant_scale
 // applies to the base path only), since it is already reading every element of x.
 //
-// Geometry: one workgroup of 4 wave64s per CU, bm = ceil(S / CUs) rows per workgroup (at least 32,
-// at most what the accumulators hold) so that the rows spread evenly over the CUs in one round, in
-// RTM = ceil(bm / 32) row tiles of 32 (rows of the last tile past bm read as zero and are not
-// written). Every wave computes all RTM row tiles for its columns: the r_pad/32 column tiles of 32
-// go to the waves round-robin, at most NC per wave, as RTM x NC tiles of v_mfma_f32_32x32x16_bf16.
+// Geometry: one workgroup of 4 wave64s per CU. The r_pad/32 column tiles of A are split into
+// `groups` column groups (1, 2 or 4, chosen by the launcher); each row block of bm rows (at least
+// 32, at most what the accumulators hold) has one workgroup per group, so the row blocks times the
+// groups spread over the CUs in one round. A workgroup holds RTM = ceil(bm / 32) row tiles of 32
+// (rows of the last tile past bm read as zero and are not written); every wave computes all RTM row
+// tiles for its columns: the group's column tiles go to the waves round-robin, at most NC per wave,
+// as RTM x NC tiles of v_mfma_f32_32x32x16_bf16. Each group writes its columns of t' and its slice of
+// the block's xs rows.
 //
 // x is read once from HBM, so this is a streaming kernel bound by how many x bytes are in flight per
 // CU. K goes through in BK-deep tiles (64, or 32 when each wave holds more than one column tile) on
@@ -153,6 +156,7 @@ struct LdCtx {
   uint32_t wave, lane;
   int k_tiles, x_copies;  // real x copies per tile for the whole workgroup
   uint32_t smem0;
+  uint32_t xs_lo, xs_hi;  // rows of the block whose xs this workgroup writes
 };
 
 // This wave's copies of A tile kt into A slot `slot` (to the spare area past the last tile).
@@ -254,7 +258,8 @@ __device__ __forceinline__ void xs_store(const LdCtx& c, const uint8_t* x0, cons
 #pragma unroll
   for (int q = 0; q < RTM; ++q) {
     const uint32_t row = (c.wave * 64 + c.lane + 256u * q) >> 3;
-    buf_store16(scale_chunk(xv[q], ps), c.xs, row * c.xs_row_bytes + cc * 16, static_cast<uint32_t>(kp) * 128);
+    const uint32_t voff = row >= c.xs_lo && row < c.xs_hi ? (row - c.xs_lo) * c.xs_row_bytes + cc * 16 : kOutOfRange;
+    buf_store16(scale_chunk(xv[q], ps), c.xs, voff, static_cast<uint32_t>(kp) * 128);
   }
 }
 
@@ -266,8 +271,18 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
 
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * p.bm;
+  // Workgroup -> (row block, column group): the groups of one row block run on one XCD (consecutive
+  // workgroups go to different XCDs), so x is fetched from HBM once for all of them.
+  const int groups = p.groups;
+  const int64_t rb = static_cast<int64_t>(blockIdx.x / (8 * groups)) * 8 + blockIdx.x % 8;
+  const int grp = static_cast<int>((blockIdx.x / 8) % groups);
+  const int64_t m0 = rb * p.bm;
+  if (m0 >= p.S) return;  // padding of the grid to whole groups of 8 row blocks
   const int64_t rows = std::min<int64_t>(p.bm, p.S - m0);  // <= 32 * RTM
+  const int ctg = p.r_pad / 32 / groups;  // column tiles of this group: [grp * ctg, grp * ctg + ctg)
+  // xs: each group of the row block writes its own slice of the rows
+  const int64_t xs_slice = (rows + groups - 1) / groups;
+  const int64_t xs_lo = std::min<int64_t>(rows, grp * xs_slice), xs_hi = std::min<int64_t>(rows, xs_lo + xs_slice);
 
   LdCtx c;
   c.wave = wave;
@@ -282,9 +297,11 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
   c.A_row_bytes = static_cast<uint32_t>(p.K_pad * 2);
   c.xs_row_bytes = static_cast<uint32_t>(p.K_pad * 2);
   c.x = buf_rsrc(p.x + m0 * p.K, static_cast<uint32_t>(rows * p.K * 2));
-  c.A = buf_rsrc(p.A, static_cast<uint32_t>(int64_t{p.r_pad} * p.K_pad * 2));
+  c.A = buf_rsrc(p.A + static_cast<int64_t>(grp) * ctg * 32 * p.K_pad, static_cast<uint32_t>(int64_t{ctg} * 32 * p.K_pad * 2));
   c.pq = buf_rsrc(p.pqs, p.pqs ? static_cast<uint32_t>(p.K * 4) : 0u);
-  c.xs = buf_rsrc(p.xs_out + m0 * p.K_pad, XS ? static_cast<uint32_t>(rows * p.K_pad * 2) : 0u);
+  c.xs = buf_rsrc(p.xs_out + (m0 + xs_lo) * p.K_pad, XS ? static_cast<uint32_t>((xs_hi - xs_lo) * p.K_pad * 2) : 0u);
+  c.xs_lo = static_cast<uint32_t>(xs_lo);
+  c.xs_hi = static_cast<uint32_t>(xs_hi);
   c.smem0 = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(smem)));
   const bool has_pqs = p.pqs != nullptr;
@@ -355,7 +372,8 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
   const float f = p.f_div_dev ? p.f / *p.f_div_dev : p.f;
   const int row_lane = (lane >> 5) * 4;
   const int R = p.r_pad;
-  const int ct = p.r_pad / 32;  // column tiles: wave w owns tiles w, w + 4, ... (< ct)
+  // this group's column tiles: wave w owns tiles w, w + 4, ... (< ctg), t' columns from grp * ctg * 32
+  uint16_t* t_grp = p.t_out + static_cast<int64_t>(grp) * ctg * 32;
 #pragma unroll
   for (int i = 0; i < RTM; ++i)
 #pragma unroll
@@ -366,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void lora_down_kernel(LoraDownParams p
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int jt = static_cast<int>(wave) + 4 * j;
-        if (jt < ct) p.t_out[row * R + jt * 32 + r32] = static_cast<uint16_t>(f32_to_bf16_hw(f * acc[i][j][r]));
+        if (jt < ctg) t_grp[row * R + jt * 32 + r32] = static_cast<uint16_t>(f32_to_bf16_hw(f * acc[i][j][r]));
       }
     }
 }
@@ -433,13 +451,41 @@ hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (cus <= 0) return hipErrorInvalidValue;
-  // rows per workgroup: spread the rows evenly over the CUs in one round (at least one row tile of
-  // 32, at most the row tiles whose accumulators fit beside the column tiles each wave holds)
-  const int nc = (p.r_pad / 32 + 3) / 4;
+  // Rows per workgroup and column groups: every workgroup copies all of its group's A tiles from L2,
+  // so a CU moves |A| / groups + bm * K * 2 * (1 + 1 / groups) bytes (x read by every group, xs written
+  // once). Short sequences split A's columns over up to 4 workgroups per row block, as long as the
+  // rows still go through in one round and the accumulators hold them; long ones keep one group.
+  const int ct_all = p.r_pad / 32;
+  const double a_bytes = static_cast<double>(p.r_pad) * p.K_pad * 2;
+  const double row_bytes = static_cast<double>(p.K) * 2;
+  int best_g = 0;
+  int64_t best_bm = 0;
+  double best_cost = 0.0;
+  for (int g = 1; g <= 4; g *= 2) {
+    if (ct_all % g != 0) continue;
+    const int nc = (ct_all / g + 3) / 4;
+    const int64_t bm_max = 32 * max_rtm(nc);
+    int64_t bm = std::max<int64_t>(32, (p.S * g + cus - 1) / cus);
+    if (bm > bm_max) {
+      if (g > 1) continue;  // the rows would need more than one round: keep the columns together
+      bm = bm_max;
+    }
+    const int64_t wgs = (p.S + bm - 1) / bm * g;
+    const double rounds = static_cast<double>((wgs + cus - 1) / cus);
+    const double cost = rounds * (a_bytes / g + bm * row_bytes * (1.0 + (p.xs_out ? 1.0 / g : 0.0)));
+    if (best_g == 0 || cost < best_cost) {
+      best_g = g;
+      best_bm = bm;
+      best_cost = cost;
+    }
+  }
   LoraDownParams q = p;
-  q.bm = std::min<int64_t>(32 * max_rtm(nc), std::max<int64_t>(32, (p.S + cus - 1) / cus));
+  q.bm = best_bm;
+  q.groups = best_g;
+  const int nc = (ct_all / best_g + 3) / 4;
   const int rtm = static_cast<int>((q.bm + 31) / 32);
-  const int64_t blocks = (p.S + q.bm - 1) / q.bm;
+  const int64_t row_blocks = (p.S + q.bm - 1) / q.bm;
+  const int64_t blocks = (row_blocks + 7) / 8 * 8 * best_g;  // row blocks padded to whole groups of 8
   switch (rtm) {
     case 1: return launch_nc<1>(q, nc, blocks, stream);
     case 2: return launch_nc<2>(q, nc, blocks, stream);

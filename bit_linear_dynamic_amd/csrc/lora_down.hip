@@ -16,8 +16,9 @@
 // as RTM x NC tiles of v_mfma_f32_32x32x16_bf16. Each group writes its columns of t' and its slice of
 // the block's xs rows.
 //
-// x is read once from HBM, so this is a streaming kernel bound by how many x bytes are in flight per
-// CU. K goes through in BK-deep tiles (64, or 32 when each wave holds more than one column tile) on
+// x is read once from HBM and xs written once, while every workgroup copies all of its group's A tiles
+// from L2 into LDS; those byte streams, not the MFMAs, set the kernel's time (without the MFMAs it
+// runs as fast; without the A copies or the xs stores, a quarter faster). K goes through in BK-deep tiles (64, or 32 when each wave holds more than one column tile) on
 // two separate rings of LDS slots, both filled by buffer->LDS copies (no registers): the adapter tile
 // A (r_pad x BK, from L2, where every workgroup reads it) one tile ahead in two slots, and the x tile
 // (RTM*32 x BK) with its BK pqs values L tiles ahead in L + 2 slots -- all the LDS the two A slots

@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 # GEMM sources they were taken with (SHA-256 prefix of the files below, in this order).
 GEMM_TRAFFIC_BYTES = 9.026e9
 GEMM_TRAFFIC_SOURCES = ("gemm_w4.hip", "gemm_w4_steps.inc", "h3q_device.hpp", "h3q_kernels.hpp", "h3q_layout.hpp")
-GEMM_TRAFFIC_SHA = "5780977989ec6389"
+GEMM_TRAFFIC_SHA = "6ada36f57eadc907"
 
 
 def gemm_traffic():

@@ -91,4 +91,47 @@ inline void tile_adapter(const uint16_t* A, const uint16_t* B, int64_t rank, int
     }
 }
 
+// ---- LoRA-down work split (lora_down.hip) ----
+// Row tiles of 32 a LoRA-down workgroup can hold with nc column tiles per wave: the RTM x nc
+// accumulator tiles (16 registers each) stay within the 256 accumulation registers.
+constexpr int lora_max_rtm(int nc) { return nc <= 2 ? 6 : (nc == 3 ? 5 : 3); }
+
+struct LoraSplit {
+  int64_t bm;       // rows per workgroup
+  int32_t groups;   // column groups of A per row block (1, 2 or 4)
+  int32_t nc;       // column tiles per wave
+  int64_t blocks;   // workgroups: row blocks padded to whole groups of 8, times groups
+};
+
+// Every workgroup copies all of its group's A tiles from L2, so a CU moves |A| / g + bm * K * 2 *
+// (1 + 1/g) bytes (x read by every group, xs written once). Among g in {1, 2, 4} dividing the column
+// tiles, take the fewest bytes per CU times rounds, where g > 1 must take the rows in one round with
+// rows that fit the accumulators (ties: the smaller g).
+inline LoraSplit lora_down_split(int64_t S, int32_t r_pad, int64_t K, int64_t K_pad, bool xs, int cus) {
+  const int ct_all = r_pad / 32;
+  const double a_bytes = static_cast<double>(r_pad) * static_cast<double>(K_pad) * 2.0;
+  const double row_bytes = static_cast<double>(K) * 2.0;
+  LoraSplit best{0, 0, 0, 0};
+  double best_cost = 0.0;
+  for (int g = 1; g <= 4; g *= 2) {
+    if (ct_all % g != 0) continue;
+    const int nc = (ct_all / g + 3) / 4;
+    const int64_t bm_max = 32 * lora_max_rtm(nc);
+    int64_t bm = (S * g + cus - 1) / cus;
+    if (bm < 32) bm = 32;
+    if (bm > bm_max) {
+      if (g > 1) continue;  // the rows would need more than one round: keep the columns together
+      bm = bm_max;
+    }
+    const int64_t row_blocks = (S + bm - 1) / bm;
+    const double rounds = static_cast<double>((row_blocks * g + cus - 1) / cus);
+    const double cost = rounds * (a_bytes / g + static_cast<double>(bm) * row_bytes * (1.0 + (xs ? 1.0 / g : 0.0)));
+    if (best.groups == 0 || cost < best_cost) {
+      best = LoraSplit{bm, g, nc, (row_blocks + 7) / 8 * 8 * g};
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 }  // namespace h3q

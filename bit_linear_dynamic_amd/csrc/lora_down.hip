@@ -45,7 +45,6 @@ namespace h3q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxRTM = 6;
 constexpr uint32_t kLdsBudget = 160 * 1024;
 constexpr int kMaxAhead = 10;            // x tiles in flight at most
 
@@ -421,9 +420,7 @@ hipError_t launch_x(const LoraDownParams& p, int64_t blocks, hipStream_t stream)
   return p.xs_out ? launch_rt<RTM, NC, true>(p, blocks, stream) : launch_rt<RTM, NC, false>(p, blocks, stream);
 }
 
-// Row tiles per workgroup allowed with NC column tiles per wave: the RTM x NC accumulator tiles
-// (16 registers each) must stay within the 256 accumulation registers.
-constexpr int max_rtm(int nc) { return nc <= 2 ? kMaxRTM : (nc == 3 ? 5 : 3); }
+constexpr int max_rtm(int nc) { return lora_max_rtm(nc); }
 
 template <int RTM, int NC>
 hipError_t launch_fit(const LoraDownParams& p, int64_t blocks, hipStream_t stream) {
@@ -452,41 +449,13 @@ hipError_t launch_lora_down(const LoraDownParams& p, hipStream_t stream) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (cus <= 0) return hipErrorInvalidValue;
-  // Rows per workgroup and column groups: every workgroup copies all of its group's A tiles from L2,
-  // so a CU moves |A| / groups + bm * K * 2 * (1 + 1 / groups) bytes (x read by every group, xs written
-  // once). Short sequences split A's columns over up to 4 workgroups per row block, as long as the
-  // rows still go through in one round and the accumulators hold them; long ones keep one group.
-  const int ct_all = p.r_pad / 32;
-  const double a_bytes = static_cast<double>(p.r_pad) * p.K_pad * 2;
-  const double row_bytes = static_cast<double>(p.K) * 2;
-  int best_g = 0;
-  int64_t best_bm = 0;
-  double best_cost = 0.0;
-  for (int g = 1; g <= 4; g *= 2) {
-    if (ct_all % g != 0) continue;
-    const int nc = (ct_all / g + 3) / 4;
-    const int64_t bm_max = 32 * max_rtm(nc);
-    int64_t bm = std::max<int64_t>(32, (p.S * g + cus - 1) / cus);
-    if (bm > bm_max) {
-      if (g > 1) continue;  // the rows would need more than one round: keep the columns together
-      bm = bm_max;
-    }
-    const int64_t wgs = (p.S + bm - 1) / bm * g;
-    const double rounds = static_cast<double>((wgs + cus - 1) / cus);
-    const double cost = rounds * (a_bytes / g + bm * row_bytes * (1.0 + (p.xs_out ? 1.0 / g : 0.0)));
-    if (best_g == 0 || cost < best_cost) {
-      best_g = g;
-      best_bm = bm;
-      best_cost = cost;
-    }
-  }
+  const LoraSplit sp = lora_down_split(p.S, p.r_pad, p.K, p.K_pad, p.xs_out != nullptr, cus);
   LoraDownParams q = p;
-  q.bm = best_bm;
-  q.groups = best_g;
-  const int nc = (ct_all / best_g + 3) / 4;
+  q.bm = sp.bm;
+  q.groups = sp.groups;
+  const int nc = sp.nc;
   const int rtm = static_cast<int>((q.bm + 31) / 32);
-  const int64_t row_blocks = (p.S + q.bm - 1) / q.bm;
-  const int64_t blocks = (row_blocks + 7) / 8 * 8 * best_g;  // row blocks padded to whole groups of 8
+  const int64_t blocks = sp.blocks;
   switch (rtm) {
     case 1: return launch_nc<1>(q, nc, blocks, stream);
     case 2: return launch_nc<2>(q, nc, blocks, stream);

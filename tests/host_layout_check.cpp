@@ -4,7 +4,8 @@
 // from the packed buffers through the layout as the comments define it, written out here a second
 // time (the inverse direction: from a caller's row to its packed tile and column), so that an index
 // slip in either the loops or this check shows as a mismatch, and any access outside the buffers as a
-// sanitizer report. Prints "ok" and exits 0 when everything matches.
+// sanitizer report. It also checks the LoRA-down work split (lora_down_split). Prints "ok" and exits 0
+// when everything matches.
 #include <cstdint>
 #include <cstdio>
 #include <random>
@@ -94,6 +95,34 @@ int check(int64_t N, int64_t K, int64_t rank, bool gate_up, std::mt19937& rng) {
 
 }  // namespace
 
+// The LoRA-down work split (lora_down_split): rows per workgroup within what the accumulators hold,
+// one round whenever the columns are split, every (row block, column group) of the workgroup mapping
+// that lora_down_kernel uses (block b: row block (b / 8g) * 8 + b % 8, group (b / 8) % g) exactly once
+// with the groups of a row block on one XCD (b % 8), and one group at the block's S = 37726.
+int check_split(int64_t S, int32_t r_pad, int64_t K, bool xs, int cus) {
+  const int64_t K_pad = (K + 63) / 64 * 64;
+  const LoraSplit sp = lora_down_split(S, r_pad, K, K_pad, xs, cus);
+  int bad = 0;
+  const int ct = r_pad / 32;
+  if (sp.groups < 1 || ct % sp.groups != 0 || sp.nc != (ct / sp.groups + 3) / 4) ++bad;
+  if (sp.bm < 32 || sp.bm > 32 * lora_max_rtm(sp.nc)) ++bad;
+  const int64_t row_blocks = (S + sp.bm - 1) / sp.bm;
+  if (sp.groups > 1 && row_blocks * sp.groups > cus) ++bad;
+  if (sp.blocks != (row_blocks + 7) / 8 * 8 * sp.groups) ++bad;
+  std::vector<char> seen(static_cast<size_t>(row_blocks * sp.groups), 0);
+  for (int64_t b = 0; b < sp.blocks; ++b) {
+    const int64_t rb = (b / (8 * sp.groups)) * 8 + b % 8, grp = (b / 8) % sp.groups;
+    if (rb % 8 != b % 8) ++bad;
+    if (rb * sp.bm >= S) continue;  // padding workgroups return at once
+    char& v = seen[static_cast<size_t>(rb * sp.groups + grp)];
+    if (v) ++bad;
+    v = 1;
+  }
+  for (char v : seen) bad += v ? 0 : 1;
+  if (bad) std::printf("lora_down_split S=%lld r_pad=%d K=%lld: %d mismatches\n", (long long)S, r_pad, (long long)K, bad);
+  return bad;
+}
+
 int main() {
   std::mt19937 rng(2024);
   int bad = 0;
@@ -103,6 +132,13 @@ int main() {
     bad += check(s[0], s[1], s[2], false, rng);
     if (s[0] % 2 == 0) bad += check(s[0], s[1], s[2], true, rng);
   }
+  for (int64_t S : {1, 31, 77, 256, 300, 1000, 8192, 16384, 37726, 37728, 65836, 140000, 4200000})
+    for (int32_t r_pad : {32, 64, 128, 160, 320, 384, 512})
+      for (int64_t K : {512, 1040, 6144, 16384})
+        for (bool xs : {true, false}) bad += check_split(S, r_pad, K, xs, 256);
+  for (int32_t r_pad : {128, 384})
+    for (int64_t K : {6144, 16384})
+      if (lora_down_split(37726, r_pad, K, K, true, 256).groups != 1) ++bad;
   if (bad) return 1;
   std::printf("ok\n");
   return 0;

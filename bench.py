@@ -546,8 +546,8 @@ def library_bf16_gemm(projs, S, device, calls=5):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
-              "(the projection shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        print("bench.py: the benchmark runs on exactly one GPU; multi-GPU runs are not supported "
+              "(the projection would shard by rows of x with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
 

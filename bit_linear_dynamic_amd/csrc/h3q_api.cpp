@@ -216,7 +216,8 @@ h3q_status workspace(int dev, hipStream_t stream, size_t need, uint8_t** out) {
 // A file-scope device array: every GPU the library runs on holds its own copy from the time the
 // library's code is loaded there until the process ends. In host code `scratch` is only a stand-in
 // for the symbol, never a device address: the address is looked up once per device, with that device
-// current, and only that pointer is handed to kernels.
+// current (when the first weight is packed there, else on the first no-allocation call), and only
+// that pointer is handed to kernels.
 static_assert(H3Q_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
 static __device__ __align__(256) uint8_t scratch[H3Q_NOALLOC_SCRATCH_BYTES];
 
@@ -314,6 +315,10 @@ h3q_status h3q_pack_weight(void* stream, const uint8_t* codes, const uint8_t* sc
                   (long long)(i / (K / 16)), (long long)(i % (K / 16)));
   int dev;
   if (h3q_status st = check_device(&dev)) return st;
+  // set-up of the device for h3q_linear_ex_noalloc: its scratch address is looked up here, outside any
+  // stream capture, so that a first no-allocation call under capture makes no runtime query
+  uint8_t* scratch_dev = nullptr;
+  if (h3q_status st = scratch_on_device(dev, &scratch_dev)) return st;
 
   auto w = new (std::nothrow) h3q_weight_s();
   if (!w) return fail(H3Q_E_NOMEM, "pack: host allocation failed");

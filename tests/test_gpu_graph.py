@@ -142,3 +142,41 @@ def test_two_streams_concurrently(projs):
         h3q.h3q_linear_swiglu(xb, pqs, gu.handle, 1, 0.5, h=hb2, stream=sb)
     torch.cuda.synchronize()
     assert torch.equal(ya, ya2) and torch.equal(hb, hb2)
+
+
+def test_noalloc_captured_without_a_warm_up_call(projs, monkeypatch):
+    """h3q_linear_ex_noalloc under capture with no eager call on the stream first (it needs no
+    workspace) and the library's allocator failing throughout: three replays, with eager calls on the
+    same fixed scratch between them, equal h3q_linear_ex's results bit for bit (W4A4 included)."""
+    qkv, gu = projs
+    S = 384
+    say(f"no-alloc capture S={S}")
+    s = torch.cuda.Stream()
+    x, pqs = _inputs(S, 2440)
+    x2, _ = _inputs(S, 2442)
+    ref = [h3q.h3q_linear_ex(x, pqs, qkv.handle, 1, 1.0),
+           h3q.h3q_linear_ex(x, None, qkv.handle, NONE, 0.0),
+           h3q.h3q_linear_ex(x, pqs, gu.handle, 1, 1.0, h3q.H3Q_ACT_NVFP4 | h3q.H3Q_EPI_SWIGLU)]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(t) for t in ref]
+    other = torch.empty_like(ref[0])
+    monkeypatch.setenv("H3Q_TEST_FAIL_ALLOC_AFTER", "0")  # any library allocation from here on fails
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        h3q.h3q_linear_ex_noalloc(x, pqs, qkv.handle, 1, 1.0, 0, out=outs[0], stream=s)
+        h3q.h3q_linear_ex_noalloc(x, None, qkv.handle, NONE, 0.0, 0, out=outs[1], stream=s)
+        h3q.h3q_linear_ex_noalloc(x, pqs, gu.handle, 1, 1.0, h3q.H3Q_ACT_NVFP4 | h3q.H3Q_EPI_SWIGLU, out=outs[2],
+                                  stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        with torch.cuda.stream(s):  # eager work on the same scratch between replays
+            h3q.h3q_linear_ex_noalloc(x2, pqs, qkv.handle, 1, 0.5, h3q.H3Q_ACT_NVFP4, out=other, stream=s)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got, want), rep
+        say(f"  replay {rep}: bit-identical to h3q_linear_ex")
